@@ -1,0 +1,113 @@
+"""Compression of one dense expert matrix to the 4:8 / E2M1 / E4M3 format and
+its exact decode.  ORACLE (test infrastructure only).
+
+Follows the paper summary page, "3.4 Implementation details" (scales are
+recomputed, then E2M1 values, sparse metadata and a scale per 32 logical
+weights are packed) and "A Sparse-quantized representation" (each group of
+eight keeps four values; 16 kept values of a 32-weight block share one scale;
+zero lies on the grid so pruned positions are feasible).  The selection of
+the support here is the hard top-4 by magnitude; the pages learn it, which is
+offline work outside this path.
+
+Byte layout of one expert W [N, K] (K % 32 == 0), row-major:
+  values [N, K/4]  two E2M1 codes per byte, the group's four kept codes in
+                   ascending position, the lower one in the low nibble
+  masks  [N, K/8]  bit i set <=> position 8*g + i is kept (popcount 4)
+  scales [N, K/32] E4M3 code of the block scale (sign 0)
+  g      fp32      global scale of the expert matrix
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from .formats import E2M1_VALUES, E4M3_VALUES, e2m1_encode, e4m3_encode
+
+E2M1_MAX = np.float32(6.0)
+E4M3_MAX = np.float32(448.0)
+
+
+@dataclasses.dataclass
+class PackedExpert:
+    values: np.ndarray   # uint8 [N, K/4]
+    masks: np.ndarray    # uint8 [N, K/8]
+    scales: np.ndarray   # uint8 [N, K/32]
+    g: np.float32
+
+    @property
+    def nbytes(self) -> int:
+        return self.values.nbytes + self.masks.nbytes + self.scales.nbytes + 4
+
+
+def support(Wd: np.ndarray) -> np.ndarray:
+    """Boolean keep-map [N, K]: in every group of 8 consecutive K positions
+    the 4 largest |w|; equal magnitudes go to the lower position."""
+    N, K = Wd.shape
+    a = np.abs(Wd.astype(np.float32)).reshape(N, K // 8, 8)
+    order = np.argsort(-a, axis=2, kind="stable")
+    keep = np.zeros_like(a, dtype=bool)
+    np.put_along_axis(keep, order[:, :, :4], True, axis=2)
+    return keep.reshape(N, K)
+
+
+def masks_of(keep: np.ndarray) -> np.ndarray:
+    N, K = keep.shape
+    bits = keep.reshape(N, K // 8, 8).astype(np.uint32) << np.arange(8, dtype=np.uint32)
+    return bits.sum(axis=2).astype(np.uint8)
+
+
+def quantize(Wd: np.ndarray) -> PackedExpert:
+    """Compress a dense fp32 [N, K] expert matrix.
+
+    All arithmetic that decides a code is done in fp32, in this order:
+      g     = amax / 2688          (2688 = 6 * 448; g = 1 if amax == 0)
+      six_g = 6 * g
+      s     = E4M3(amax_32 / six_g)             per 32-position block
+      q     = E2M1(w / (value(s) * g))          per kept weight
+    """
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    N, K = Wd.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    keep = support(Wd)
+    a = np.abs(Wd)
+    amax = np.float32(a[keep].max()) if a.size else np.float32(0)
+    g = np.float32(amax / np.float32(2688.0)) if amax > 0 else np.float32(1.0)
+    six_g = np.float32(np.float32(6.0) * g)
+    amax_blk = np.where(keep, a, np.float32(0)).reshape(N, K // 32, 32).max(axis=2)
+    s_code = e4m3_encode((amax_blk / six_g).astype(np.float32))
+    s_val = E4M3_VALUES[s_code].astype(np.float32)
+    sg = (s_val * g).astype(np.float32)                      # [N, K/32]
+    sg_full = np.repeat(sg, 32, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sg_full > 0, Wd / np.where(sg_full > 0, sg_full, 1), 0).astype(np.float32)
+    codes = e2m1_encode(q)                                   # [N, K]
+    kept = codes.reshape(N, K // 8, 8)[keep.reshape(N, K // 8, 8)].reshape(N, K // 8, 4)
+    kept = kept.astype(np.uint8)
+    values = np.empty((N, K // 8, 2), np.uint8)
+    values[:, :, 0] = kept[:, :, 0] | (kept[:, :, 1] << 4)
+    values[:, :, 1] = kept[:, :, 2] | (kept[:, :, 3] << 4)
+    return PackedExpert(values.reshape(N, K // 4), masks_of(keep), s_code, g)
+
+
+def decode(p: PackedExpert, include_global: bool = True) -> np.ndarray:
+    """Dense float64 [N, K] matrix the packed expert stands for:
+    w[n, 8g+i] = E2M1(c_j) * E4M3(s_b) * g at the j-th set bit i of the mask,
+    0 elsewhere.  Exact in float64."""
+    N = p.masks.shape[0]
+    K = p.masks.shape[1] * 8
+    bits = ((p.masks[:, :, None].astype(np.uint32) >> np.arange(8)) & 1).astype(bool)
+    if (bits.sum(axis=2) != 4).any():
+        raise ValueError("every mask byte must have exactly four bits set")
+    v = p.values.reshape(N, K // 8, 2)
+    codes4 = np.stack([v[:, :, 0] & 15, v[:, :, 0] >> 4, v[:, :, 1] & 15, v[:, :, 1] >> 4],
+                      axis=2)                                  # [N, K/8, 4]
+    rank = np.clip(np.cumsum(bits, axis=2) - 1, 0, 3)          # index j of each set bit
+    code = np.take_along_axis(codes4, rank, axis=2)
+    val = np.where(bits, E2M1_VALUES[code], 0.0).reshape(N, K)
+    scale = np.repeat(E4M3_VALUES[p.scales], 32, axis=1)
+    w = val * scale
+    if include_global:
+        w = w * np.float64(p.g)
+    return w

@@ -1,0 +1,345 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics
+fix, written so that each takes the oracle module as an argument.  The
+`test_oracle_*` files run them on the real oracle; `test_oracle_mutations`
+runs them on copies of the oracle with one planted mistake each and expects
+a failure, which shows the pins would catch that mistake."""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- formats
+
+def pin_e2m1_grid(O):
+    """All 16 E2M1 codes equal the OCP MX FP4 table (golden fixture)."""
+    for code, val in _lines("e2m1_grid.txt"):
+        want = float(val)
+        got = O.E2M1_VALUES[int(code)]
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+
+
+def pin_e4m3_table(O):
+    """All 256 E4M3 codes equal torch's float8_e4m3fn cast (library cross
+    check) and the fixture's selected points."""
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.E4M3_VALUES
+    assert np.array_equal(np.isnan(lib), np.isnan(ours))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(lib[ok], ours[ok])
+    for code, val in _lines("e4m3_points.txt"):
+        got = O.E4M3_VALUES[int(code, 16)]
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val), (code, got, val)
+
+
+def pin_e4m3_encode(O, n=20000, seed=0):
+    """Encoding = torch's RNE float32->float8_e4m3fn cast below 448 (library
+    cross check) and saturation to 448 above it."""
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([
+        np.exp(rng.uniform(np.log(1e-4), np.log(500.0), n)).astype(np.float32),
+        # exact midpoints between neighbouring codes (ties)
+        ((O.E4M3_VALUES[1:0x7E] + O.E4M3_VALUES[2:0x7F]) / 2).astype(np.float32),
+        np.float32([0.0, 448.0, 464.0, 1e6, 2.0 ** -10, 3 * 2.0 ** -11])])
+    codes = O.e4m3_encode(x)
+    below = x < 448
+    ref = torch.from_numpy(x[below]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[below], ref)
+    assert (codes[~below] == 0x7E).all()
+
+
+def pin_e2m1_encode(O, n=20000, seed=1):
+    """Encoding picks a nearest grid value (brute force over all 8
+    magnitudes), ties to the even code, saturation at 6, zero as +0, and the
+    tie cases of round-half-to-even."""
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6,
+            -0.25: 0, -0.75: 10, -1.25: 10, -1.75: 12, -2.5: 12, -3.5: 14, -5.0: 14,
+            6.5: 7, 100.0: 7, -7.0: 15, 0.0: 0, -0.0: 0, 0.1: 0, -0.1: 0, 0.3: 1}
+    xs = np.float32(list(ties))
+    assert O.e2m1_encode(xs).tolist() == list(ties.values())
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-8, 8, n).astype(np.float32)
+    c = O.e2m1_encode(x)
+    mags = np.float64([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for xi, ci in zip(x.astype(np.float64), c):
+        v = O.E2M1_VALUES[ci]
+        best = np.min(np.abs(np.abs(xi) - mags))
+        if abs(xi) <= 6:
+            assert abs(abs(xi) - abs(v)) == best, (xi, ci)
+        else:
+            assert abs(v) == 6
+        if v != 0:
+            assert np.sign(v) == np.sign(xi)
+        else:
+            assert ci == 0
+
+
+def pin_bf16_round(O, n=20000, seed=2):
+    """bf16 rounding of fp32 inputs equals torch's RNE cast; explicit ties."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * np.exp(rng.uniform(-20, 20, n))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(x.astype(np.float64)), ref)
+    assert O.bf16_round(1 + 2.0 ** -8) == 1.0                      # tie -> even
+    assert O.bf16_round(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6        # tie -> even
+    assert O.bf16_round(1 + 2.0 ** -8 + 2.0 ** -30) == 1 + 2.0 ** -7
+
+
+# ---------------------------------------------------------------- packing
+
+def _hex(tokens):
+    return np.array([int(t, 16) for t in tokens], np.uint8)
+
+
+def pin_quant_fixture(O):
+    """The hand-derived 2 x 64 compression (tests/golden/quant_rows.txt)."""
+    d = {ln[0]: ln[1:] for ln in _lines("quant_rows.txt")}
+    W = np.array([[float(v) for v in d["w0"]], [float(v) for v in d["w1"]]], np.float32)
+    p = O.quantize(W)
+    assert float(p.g) == float(d["g"][0])
+    for r in range(2):
+        assert np.array_equal(p.masks[r], _hex(d[f"masks{r}"])), (r, p.masks[r])
+        assert np.array_equal(p.values[r], _hex(d[f"values{r}"])), (r, p.values[r])
+        assert np.array_equal(p.scales[r], _hex(d[f"scales{r}"])), (r, p.scales[r])
+    # decoded values, derived by hand from the codes: q * s * g
+    u, v = 0.109375, 36 * 2.0 ** -12
+    want0 = ([6 * u, 0, 4 * u, 0, 0, 0, 2 * u, 0] + [u, -u, u, -u, 0, 0, 0, 0] +
+             [0, 0, 0, 0, u, -u, 4 * u, -2 * u] + [0.5 * u, 0, -0.5 * u, 0, 0, 0, 0, 0] +
+             [6 * v, 1.5 * v, 0, 0, 0, 0, -3 * v, 0.5 * v] + [0] * 24)
+    dec = O.decode(p)
+    assert np.array_equal(dec[0], np.float64(want0))
+    assert np.array_equal(dec[1], -np.float64(want0))
+
+
+def pin_support_bruteforce(O, seed=3):
+    """The kept set of every group is the unique 4-subset whose members all
+    beat every dropped position (|w| larger, or equal and lower position),
+    found by enumerating all 70 subsets."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((6, 64)).astype(np.float32)
+    W[0, :8] = 1.0          # all equal
+    W[1, 8:16] = [2, -2, 1, 1, -1, 1, 0, 0]
+    W[2, :8] = 0.0
+    keep = O.support(W)
+    a = np.abs(W)
+    for n in range(W.shape[0]):
+        for g in range(8):
+            grp = a[n, 8 * g:8 * g + 8]
+            winners = []
+            for S in itertools.combinations(range(8), 4):
+                rest = [j for j in range(8) if j not in S]
+                if all(grp[i] > grp[j] or (grp[i] == grp[j] and i < j) for i in S for j in rest):
+                    winners.append(S)
+            assert len(winners) == 1
+            got = tuple(np.nonzero(keep[n, 8 * g:8 * g + 8])[0])
+            assert got == winners[0], (n, g, got, winners)
+
+
+def pin_masks_and_layout(O, seed=4):
+    """Every mask byte has popcount 4; a large random matrix realises all 70
+    valid masks, the six paired patterns among them; packed size is 13/32
+    byte per logical weight plus the fp32 global scale (golden layout)."""
+    d = {ln[0]: ln[1:] for ln in _lines("layout.txt")}
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((256, 512)) * 0.02).astype(np.float32)
+    p = O.quantize(W)
+    pc = np.unpackbits(p.masks[..., None], axis=-1).sum(-1)
+    assert (pc == 4).all()
+    seen = set(np.unique(p.masks).tolist())
+    assert len(seen) == int(d["valid_mask_count"][0])
+    assert {int(x, 16) for x in d["paired_patterns"]} <= seen
+    N, K = W.shape
+    bpw = float(d["mask_bits_per_weight"][0])
+    assert p.nbytes == N * K * bpw / 8 + 4
+    assert p.values.nbytes + p.masks.nbytes + p.scales.nbytes == N * K // 32 * int(d["mask_bytes_per_32"][0])
+    # the pages' paired format: 4-bit index instead of the 8-bit mask
+    paired = ((4 * 4 + int(d["paired_index_bits"][0])) * 4 + 8) / 32
+    assert paired == float(d["paired_bits_per_weight"][0])
+
+
+def pin_quant_nearest(O, seed=5):
+    """Every decoded kept weight is a nearest point of the scaled E2M1 grid
+    (brute force over all grid values) to the input, unless it saturates;
+    every block scale is a nearest E4M3 value to amax_32/(6g) (brute force
+    over all 127 finite non-negative codes); dropped positions decode to 0."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((8, 128)) * 0.02).astype(np.float32)
+    W[3, 40] = 0.5                                  # an outlier
+    p = O.quantize(W)
+    dec = O.decode(p, include_global=False)
+    keep = O.support(W)
+    g = np.float64(p.g)
+    assert (dec[~keep] == 0).all()
+    e4 = O.E4M3_VALUES[:0x7F]
+    grid = np.float64([0, .5, 1, 1.5, 2, 3, 4, 6])
+    grid = np.concatenate([-grid[::-1], grid])
+    for n in range(W.shape[0]):
+        for b in range(W.shape[1] // 32):
+            blk = W[n, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.max(np.abs(blk))
+            target = np.float32(np.float32(amax) / np.float32(np.float32(6) * p.g))
+            s = O.E4M3_VALUES[p.scales[n, b]]
+            assert abs(s - target) == np.min(np.abs(e4 - target)) or (target > 448 and s == 448)
+            sg = np.float32(np.float32(s) * p.g)
+            for i in range(32):
+                if not keep[n, 32 * b + i]:
+                    continue
+                q = np.float64(np.float32(np.float32(blk[i]) / sg)) if sg > 0 else 0.0
+                got = dec[n, 32 * b + i] / s if s else 0.0
+                if abs(q) <= 6:
+                    assert abs(q - got) == np.min(np.abs(grid - q)), (n, b, i, q, got)
+                else:
+                    assert got == np.sign(q) * 6
+
+
+# ---------------------------------------------------------------- routing
+
+def pin_route_bruteforce(O, seed=6):
+    """Offsets and permutation equal a plain loop: for each expert in turn,
+    the flat indices that chose it, in increasing order."""
+    rng = np.random.default_rng(seed)
+    for E, M in [(5, 40), (16, 300), (3, 1), (7, 7000)]:
+        ids = rng.integers(0, E, M).astype(np.int32)
+        if M > 10:
+            ids[: M // 3] = 1                       # many duplicates
+        off, perm, inv = O.route(ids, E)
+        p, o = [], [0]
+        for e in range(E):
+            for i in range(M):
+                if ids[i] == e:
+                    p.append(i)
+            o.append(len(p))
+        assert off.tolist() == o
+        assert perm.tolist() == p
+        for r in range(M):
+            assert inv[perm[r]] == r
+
+
+# ---------------------------------------------------------------- GEMM
+
+def _to_fraction(x):
+    return Fraction(float(x))
+
+
+def pin_gemm_exact(O, seed=7):
+    """Grouped GEMM against exact rational arithmetic on tiny inputs: bf16
+    tokens and decoded weights are dyadic, so Fraction sums are exact; the
+    float64 oracle must lie within gamma_K * sum |x||w| of them."""
+    rng = np.random.default_rng(seed)
+    E, N, K, T, k = 3, 6, 64, 5, 2
+    Ws = [O.quantize((rng.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in range(E)]
+    dense = [O.decode(p) for p in Ws]
+    x = torch.randn(T, K, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    x = x.to(torch.float64).numpy()
+    ids = np.array([[0, 2], [2, 1], [0, 1], [2, 0], [1, 2]], np.int32).reshape(-1)
+    off, perm, inv = O.route(ids, E)
+    xr = O.permute(x, perm, k)
+    Y = O.grouped_gemm(xr, off, lambda e: dense[e])
+    u = 2.0 ** -53
+    gamma = K * u / (1 - K * u)
+    for r in range(T * k):
+        e = ids[perm[r]]
+        assert np.array_equal(xr[r], x[perm[r] // k])
+        for n in range(N):
+            exact = sum(_to_fraction(xr[r, kk]) * _to_fraction(dense[e][n, kk]) for kk in range(K))
+            bound = gamma * float(sum(abs(_to_fraction(xr[r, kk]) * _to_fraction(dense[e][n, kk]))
+                                      for kk in range(K)))
+            assert abs(Fraction(float(Y[r, n])) - exact) <= Fraction(bound) + Fraction(1, 2 ** 1074), (r, n)
+
+
+def pin_gemm_invariances(O, seed=8):
+    """Permuting tokens permutes routed rows consistently; relabelling
+    experts permutes offsets; scaling X by 2^p scales Y by 2^p exactly."""
+    rng = np.random.default_rng(seed)
+    E, N, K, T, k = 4, 16, 96, 9, 2
+    Ws = [O.decode(O.quantize((rng.standard_normal((N, K)) * 0.02).astype(np.float32)))
+          for _ in range(E)]
+    x = np.float64(rng.standard_normal((T, K)).astype(np.float32))
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+
+    def run(x, ids, Ws):
+        off, perm, inv = O.route(ids.reshape(-1), len(Ws))
+        Y = O.grouped_gemm(O.permute(x, perm, k), off, lambda e: Ws[e])
+        return off, O.unpermute(Y, inv, None, x.shape[0], k)
+
+    off, flat = run(x, ids, Ws)
+    sigma = rng.permutation(T)
+    off2, flat2 = run(x[sigma], ids[sigma], Ws)
+    assert np.array_equal(off, off2)
+    assert np.allclose(flat2.reshape(T, k, N), flat.reshape(T, k, N)[sigma], rtol=1e-12, atol=0)
+    tau = rng.permutation(E)                       # expert e becomes tau[e]
+    Wt = [None] * E
+    for e in range(E):
+        Wt[tau[e]] = Ws[e]
+    off3, flat3 = run(x, tau[ids].astype(np.int32), Wt)
+    counts = np.diff(off)
+    assert np.array_equal(np.diff(off3)[tau], counts)
+    assert np.allclose(flat3, flat, rtol=1e-12, atol=0)
+    _, flat4 = run(x * 2.0 ** 5, ids, Ws)
+    assert np.array_equal(flat4, flat * 2.0 ** 5)
+    # each routed row equals the dense product with that token and expert
+    for t in range(T):
+        for j in range(k):
+            want = np.array([sum(x[t, kk] * Ws[ids[t, j]][n, kk] for kk in range(K)) for n in range(N)])
+            assert np.allclose(flat[t * k + j], want, rtol=1e-12, atol=1e-300)
+
+
+# ---------------------------------------------------------------- combine and SwiGLU
+
+def pin_unpermute(O, seed=9):
+    """k = 1 with unit weights inverts dispatch exactly; the weighted combine
+    equals a plain loop over (t, j)."""
+    rng = np.random.default_rng(seed)
+    T, E, N = 11, 4, 8
+    x = rng.standard_normal((T, N))
+    ids = rng.integers(0, E, T).astype(np.int32)
+    off, perm, inv = O.route(ids, E)
+    xr = O.permute(x, perm, 1)
+    assert np.array_equal(O.unpermute(xr, inv, np.ones(T, np.float32), T, 1), x)
+    assert np.array_equal(O.unpermute(xr, inv, None, T, 1), x)
+    k = 3
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).reshape(-1).astype(np.int32)
+    off, perm, inv = O.route(ids, E)
+    Y = rng.standard_normal((T * k, N))
+    w = rng.random(T * k).astype(np.float32)
+    out = O.unpermute(Y, inv, w, T, k)
+    for t in range(T):
+        want = np.zeros(N)
+        for j in range(k):
+            r = list(perm).index(t * k + j)
+            want = want + np.float64(w[t * k + j]) * Y[r]
+        assert np.array_equal(out[t], want)
+
+
+def pin_swiglu(O):
+    """silu against torch's float64 silu and closed forms; gate = first half."""
+    x = np.linspace(-30, 30, 2001)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(O.silu(x), ref, rtol=1e-14, atol=1e-300)
+    assert O.silu(0.0) == 0.0
+    assert abs(O.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert O.silu(-800.0) == 0.0
+    y1 = np.array([[0.0, 1.0, 2.0, 3.0]])          # gate [0, 1], up [2, 3]
+    h = O.swiglu(y1)
+    assert np.allclose(h, [[0.0, 3.0 / (1.0 + math.exp(-1.0))]], rtol=1e-15)
+
+
+ALL_PINS = [pin_e2m1_grid, pin_e4m3_table, pin_e4m3_encode, pin_e2m1_encode,
+            pin_bf16_round, pin_quant_fixture, pin_support_bruteforce,
+            pin_masks_and_layout, pin_quant_nearest, pin_route_bruteforce,
+            pin_gemm_exact, pin_gemm_invariances, pin_unpermute, pin_swiglu]

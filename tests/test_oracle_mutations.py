@@ -1,0 +1,122 @@
+"""Planted mistakes in the oracle (on the CPU only): each plausible slip must
+make at least one pin fail, which shows the pins are sharp enough."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.formats
+import oracle.moe
+import oracle.pack
+import oracle.route
+import pins
+
+
+def _ns(**over):
+    ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("_")})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _fails(pin, O):
+    with pytest.raises(AssertionError):
+        pin(O)
+
+
+def test_wrong_e2m1_entry(monkeypatch):
+    bad = oracle.E2M1_VALUES.copy()
+    bad[5] = 2.5                                   # 3.0 mistyped
+    _fails(pins.pin_e2m1_grid, _ns(E2M1_VALUES=bad))
+
+
+def test_e4m3_wrong_bias():
+    bad = np.array([oracle.e4m3_decode(c) * 2 for c in range(256)])
+    _fails(pins.pin_e4m3_table, _ns(E4M3_VALUES=bad))
+
+
+def test_e2m1_ties_away_from_zero(monkeypatch):
+    def enc(x):
+        x = np.asarray(x, np.float64)
+        shape = x.shape
+        x = x.reshape(-1)
+        mags = np.float64([0, .5, 1, 1.5, 2, 3, 4, 6])
+        d = np.abs(np.abs(x)[:, None] - mags[None])
+        # last minimum instead of the even one: ties go up
+        m = (d.shape[1] - 1 - np.argmin(d[:, ::-1], axis=1)).astype(np.uint8)
+        return (m | (((x < 0) & (m != 0)).astype(np.uint8) << 3)).astype(np.uint8).reshape(shape)
+    _fails(pins.pin_e2m1_encode, _ns(e2m1_encode=enc))
+    monkeypatch.setattr(oracle.pack, "e2m1_encode", enc)
+    _fails(pins.pin_quant_fixture, oracle)
+
+
+def test_nibble_order_swapped(monkeypatch):
+    real = oracle.pack.quantize
+
+    def swapped(W):
+        p = real(W)
+        v = p.values
+        p.values = ((v >> 4) | (v << 4)).astype(np.uint8)
+        return p
+    _fails(pins.pin_quant_fixture, _ns(quantize=swapped))
+
+
+def test_scale_without_six(monkeypatch):
+    monkeypatch.setattr(oracle.pack, "e4m3_encode",
+                        lambda x: oracle.formats.e4m3_encode(np.asarray(x) * 6))
+    _fails(pins.pin_quant_fixture, oracle)
+
+
+def test_support_ties_to_higher_position():
+    def sup(W):
+        N, K = W.shape
+        a = np.abs(W.astype(np.float32)).reshape(N, K // 8, 8)[:, :, ::-1]
+        order = 7 - np.argsort(-a, axis=2, kind="stable")
+        keep = np.zeros_like(a, dtype=bool)
+        np.put_along_axis(keep, order[:, :, :4], True, axis=2)
+        return keep.reshape(N, K)
+    _fails(pins.pin_support_bruteforce, _ns(support=sup))
+
+
+def test_route_unstable():
+    def rt(ids, E):
+        off, perm, inv = oracle.route(ids, E)
+        ids = np.asarray(ids)
+        perm = np.argsort(ids * (len(ids) + 1) - np.arange(len(ids)), kind="stable").astype(np.int32)
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm))
+        return off, perm, inv
+    _fails(pins.pin_route_bruteforce, _ns(route=rt))
+
+
+def test_gemm_transposed_operand(monkeypatch):
+    def gg(xr, off, weight_of):
+        return oracle.grouped_gemm(xr, off, lambda e: weight_of(e)[:, ::-1])
+    _fails(pins.pin_gemm_exact, _ns(grouped_gemm=gg))
+
+
+def test_gemm_dropped_global_scale(monkeypatch):
+    real = oracle.pack.decode
+    monkeypatch.setattr(oracle.pack, "decode", lambda p, include_global=True: real(p, False))
+    _fails(pins.pin_quant_fixture, _ns(decode=oracle.pack.decode))
+
+
+def test_unpermute_weight_index():
+    def up(y, inv, w, T, k):
+        if w is None:
+            return oracle.unpermute(y, inv, None, T, k)
+        w = np.asarray(w).reshape(k, T).T.reshape(-1) if T != k else w[::-1]
+        return oracle.unpermute(y, inv, w, T, k)
+    _fails(pins.pin_unpermute, _ns(unpermute=up))
+
+
+def test_swiglu_halves_swapped():
+    def sw(y1):
+        n2 = y1.shape[1] // 2
+        return oracle.silu(y1[:, n2:]) * y1[:, :n2]
+    _fails(pins.pin_swiglu, _ns(swiglu=sw))
+
+
+def test_silu_sign():
+    _fails(pins.pin_swiglu, _ns(silu=lambda x: np.asarray(x) / (1 + np.exp(np.asarray(x)))))

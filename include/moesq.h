@@ -1,0 +1,201 @@
+/*
+ * moesq.h -- C ABI of the grouped 4:8 sparse-FP4 expert GEMM library
+ * (libmoesq.so, built for AMD Instinct MI355X / gfx950).
+ *
+ * Method: Hardware-Native Joint Sparse-Quantization for Trillion-Scale
+ * Mixture-of-Experts (paper summary page).  The library runs the expert half
+ * of a MoE layer whose expert weights are stored 4:8 semi-structured sparse
+ * with E2M1 (FP4) values and E4M3 block scales:
+ *
+ *   route      expert offsets + stable gather permutation      ("3.4 Implementation details":
+ *                                                               one launch covers every
+ *                                                               routing-dependent expert problem)
+ *   permute    dispatch: gather routed token rows               ("D.1 Implementation details")
+ *   grouped_spgemm  Y = X_routed * W_e^T for every expert, the  ("3.4 Implementation details",
+ *              weights decoded in registers, optional SwiGLU    "A Sparse-quantized representation",
+ *              epilogue                                         "D.1 Implementation details")
+ *   unpermute  combine: back to token order, optionally         ("D.1", "D.3 End-to-end serving
+ *              weighted by the router                            benchmark")
+ *   pack_weights  compress dense fp32 experts into the format   ("3.4 Implementation details":
+ *                                                               E2M1 values, sparse metadata and
+ *                                                               one scale per 32 logical weights)
+ *
+ * Conventions (every call):
+ *   - Pointers are DEVICE pointers unless marked "host".  bf16 tensors are
+ *     passed as uint16_t (raw bf16 bits).  All tensors are dense row-major.
+ *   - The caller owns every buffer.  The library allocates and frees no
+ *     device memory, never synchronises the stream, and enqueues all work on
+ *     `stream` (0 = the null stream).
+ *   - A call checks its arguments on the host first; on a bad argument it
+ *     returns an error and launches nothing.  A failed launch returns
+ *     MOESQ_ERR_HIP.  moesq_last_error() gives a detail string for the last
+ *     error of the calling thread.
+ *   - Kernels are memory-safe for any bytes in the inputs: out-of-range ids,
+ *     offsets or permutation entries are clamped or skipped, never
+ *     dereferenced.  Results for such inputs are unspecified.
+ *   - Calls that share buffers and overlap on different streams race; calls
+ *     on one stream run in order.
+ */
+#ifndef MOESQ_H
+#define MOESQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOESQ_OK = 0,
+  MOESQ_ERR_NULL = -1,      /* a required pointer is NULL                     */
+  MOESQ_ERR_SHAPE = -2,     /* a size or count is outside the supported range  */
+  MOESQ_ERR_WORKSPACE = -3, /* workspace missing or smaller than required      */
+  MOESQ_ERR_LAYOUT = -4,    /* unknown weight layout                           */
+  MOESQ_ERR_HIP = -5,       /* a HIP runtime call or kernel launch failed      */
+  MOESQ_ERR_ARG = -6        /* any other invalid argument                      */
+} moesq_status_t;
+
+typedef enum {
+  MOESQ_EPI_NONE = 0,   /* y[r][n] = bf16(g_e * acc[r][n])                              */
+  MOESQ_EPI_SWIGLU = 1  /* y[r][c] = bf16(silu(g_e*acc[r][c]) * g_e*acc[r][c+N/2]), c<N/2 */
+} moesq_epilogue_t;
+
+#define MOESQ_LAYOUT_CANONICAL 0
+
+/* Limits of this build. */
+#define MOESQ_MAX_EXPERTS 1024
+
+/*
+ * Compressed expert weights, canonical layout.  For expert e (0 <= e < E),
+ * W_e is N x K (output features x contraction), K % 32 == 0.  Source of the
+ * format: "A Sparse-quantized representation" (groups of eight keep four
+ * values; 16 kept values share one scale; zero is on the grid) and "Storage
+ * layout"; this library stores an unconstrained 8-bit mask per group, i.e.
+ * 13/32 byte per logical weight.
+ *
+ *   values [E][N][K/4]  E2M1 codes, two per byte.  The four kept codes of a
+ *                       group of 8 come in ascending K position; the lower
+ *                       position sits in the low nibble.
+ *   masks  [E][N][K/8]  bit i set <=> position 8*g+i of group g is kept.
+ *                       Exactly four bits must be set (caller contract).
+ *   scales [E][N][K/32] E4M3 block scale of positions [32b, 32b+32).
+ *   global_scale [E]    fp32 scale of the whole expert matrix.
+ *
+ *   W_e[n][8g+i] = E2M1(code_j) * E4M3(scale_b) * global_scale[e] at the j-th
+ *   set bit i of mask byte g, and 0 at cleared bits.
+ *
+ * The struct itself is a host object; its pointers are device pointers.
+ * Buffers are read-only to the library except in moesq_pack_weights.
+ */
+typedef struct {
+  const uint8_t *values;
+  const uint8_t *masks;
+  const uint8_t *scales;
+  const float *global_scale;
+  int32_t E, N, K;
+  int32_t layout; /* MOESQ_LAYOUT_CANONICAL */
+} moesq_weights_t;
+
+/*
+ * Routing plan (stable counting sort of the flat top-k ids).
+ *   topk_ids        [T*k] int32, flat index i = t*k + j; ids in [0, E).
+ *   expert_offsets  [E+1] int32 out: offsets[e] = first routed row of expert e
+ *                   (the number of valid ids below e); offsets[E] = T*k.
+ *   perm            [T*k] int32 out: perm[r] = flat index i of routed row r;
+ *                   rows are ordered by (expert, i), so the order is stable.
+ *   inv_perm        [T*k] int32 out: inv_perm[perm[r]] = r.
+ *   ws, ws_bytes    workspace; moesq_route_workspace_bytes() bytes (may be 0).
+ * Limits: 1 <= E <= MOESQ_MAX_EXPERTS, 1 <= k <= E, T >= 0, T*k < 2^31.
+ * Ids outside [0, E) are not routed: they get inv_perm = -1 and are left out
+ * of the offsets (offsets[E] then counts only valid ids).
+ * Results are bit-identical on every run.
+ */
+moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                           int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moesq_route_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/*
+ * Dispatch: x_routed[r][:] = x[perm[r] / k][:].
+ *   x         [T][K] bf16;  perm [T*k] int32 (from moesq_route);
+ *   x_routed  [T*k][K] bf16 out.  Rows with perm[r] outside [0, T*k) are zero.
+ * Limits: K % 8 == 0, K > 0.
+ */
+moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, int32_t k,
+                             int32_t K, uint16_t *x_routed, hipStream_t stream);
+
+/*
+ * Grouped sparse GEMM over all experts in one pass:
+ *   for every expert e and routed row r in [offsets[e], offsets[e+1]):
+ *     acc[r][n] = sum_k x_routed[r][k] * W~_e[n][k]   (fp32 accumulation, the
+ *                 decoded bf16 weights W~ = E2M1*E4M3 are exact)
+ *     epilogue NONE:   y[r][n] = bf16_rne(global_scale[e] * acc[r][n]),  y is [M][N]
+ *     epilogue SWIGLU: y[r][c] = bf16_rne(silu(g*acc[r][c]) * g*acc[r][c+N/2]),
+ *                      c < N/2, y is [M][N/2]  (gate = first half of W rows)
+ *   x_routed        [M][K] bf16, expert-sorted rows (moesq_permute output)
+ *   expert_offsets  [E+1] int32 (moesq_route output); offsets are clamped to [0, M]
+ *   w               host pointer to the weight descriptor
+ *   ws, ws_bytes    workspace; moesq_spgemm_workspace_bytes() bytes (may be 0)
+ * Rows of y outside every expert range are not written.
+ * Limits: K % 32 == 0, N % 16 == 0 (SWIGLU: N % 32 == 0), E <= MOESQ_MAX_EXPERTS,
+ *         M >= 0.
+ */
+moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed, const int32_t *expert_offsets,
+                                    int32_t M, const moesq_weights_t *w, int32_t epilogue,
+                                    uint16_t *y, void *ws, size_t ws_bytes, hipStream_t stream);
+size_t moesq_spgemm_workspace_bytes(int32_t M, const moesq_weights_t *w);
+
+/*
+ * Combine.
+ *   topk_weights != NULL: out[t][:] = bf16_rne( sum_{j<k} w[t*k+j] * y[inv_perm[t*k+j]][:] ),
+ *                         fp32 accumulation in j order; out is [T][N].
+ *   topk_weights == NULL: out[i][:] = y[inv_perm[i]][:] for i < T*k (flat order); out is [T*k][N].
+ *   y [T*k][N] bf16 (routed order), inv_perm [T*k] int32, topk_weights [T*k] fp32.
+ * Entries of inv_perm outside [0, T*k) contribute zero.
+ * Limits: N % 8 == 0, N > 0.
+ */
+moesq_status_t moesq_unpermute(const uint16_t *y, const int32_t *inv_perm,
+                               const float *topk_weights, int32_t T, int32_t k, int32_t N,
+                               uint16_t *out, hipStream_t stream);
+
+/*
+ * Compress dense fp32 experts into the canonical layout above
+ * ("3.4 Implementation details": scales recomputed, then E2M1 values, sparse
+ * metadata and a scale per 32 logical weights packed).  Per expert:
+ *   support  keep the 4 largest |w| of every group of 8; equal |w| -> lower position
+ *   g        = amax / 2688 in fp32 (2688 = 6*448), g = 1 if amax == 0
+ *   s_b      = E4M3 round-to-nearest-even, saturating at 448, of amax_b / (6*g)
+ *   q        = E2M1 round-to-nearest-even, saturating at 6, of w / (E4M3(s_b)*g);
+ *              zero is encoded +0; q = 0 when E4M3(s_b)*g == 0
+ *   dense [E][N][K] fp32 in; values/masks/scales/global_scale out (sizes above).
+ * Dense inputs must be finite.  global_scale doubles as the scratch of the
+ * per-expert maximum, so it must not alias the other buffers.
+ * Limits: K % 32 == 0, N >= 1, E >= 1.
+ */
+moesq_status_t moesq_pack_weights(const float *dense, int32_t E, int32_t N, int32_t K,
+                                  uint8_t *values, uint8_t *masks, uint8_t *scales,
+                                  float *global_scale, hipStream_t stream);
+
+/*
+ * Decode one expert to dense bf16 WITHOUT the global scale:
+ *   dense[n][k] = E2M1(code) * E4M3(scale) (exact in bf16) or 0.
+ * Uses the same in-register decoder as moesq_grouped_spgemm; meant for
+ * checking and debugging.  dense is [N][K] bf16.  0 <= expert < E.
+ */
+moesq_status_t moesq_decode_weights(const moesq_weights_t *w, int32_t expert, uint16_t *dense,
+                                    hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *moesq_status_string(moesq_status_t st);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *moesq_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t moesq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOESQ_H */

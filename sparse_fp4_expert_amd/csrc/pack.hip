@@ -1,0 +1,201 @@
+// Compression of dense fp32 experts into the 4:8 / E2M1 / E4M3 layout, and a
+// decode-to-dense kernel that exercises the GEMM's in-register decoder.
+//
+// Paper summary page, "3.4 Implementation details": scales are recomputed,
+// then E2M1 values, sparse metadata and a UE4M3 scale per 32 logical weights
+// are packed.  "A Sparse-quantized representation": 4 of every 8 weights are
+// kept, the 16 kept values of a 32-weight block share the scale, and zero is
+// on the grid.  The support here is the hard top-4 by magnitude.
+//
+// Steps (one expert matrix at a time, every decision in fp32):
+//   zero      amax[e] = 0
+//   amax      amax[e] = max |w| over the expert (atomicMax on the fp32 bits,
+//             exact and order-free for non-negative values)
+//   finalize  g[e] = amax / 2688 (= 6*448), or 1 when amax == 0
+//   quantize  one thread per group of 8; four neighbouring lanes form a
+//             32-weight block and share its maximum through lane shuffles
+#include "common.hpp"
+
+namespace moesq {
+
+constexpr int PACK_THREADS = 256;
+
+__global__ void fill_u32_kernel(uint32_t *p, int n, uint32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(PACK_THREADS) void amax_kernel(const float4 *__restrict__ dense,
+                                                            long long per_expert4,
+                                                            uint32_t *amax_bits) {
+  const int e = blockIdx.y;
+  const float4 *src = dense + (long long)e * per_expert4;
+  uint32_t m = 0;
+  for (long long i = (long long)blockIdx.x * PACK_THREADS + threadIdx.x; i < per_expert4;
+       i += (long long)gridDim.x * PACK_THREADS) {
+    const float4 v = src[i];
+    m = max(m, __float_as_uint(fabsf(v.x)));
+    m = max(m, __float_as_uint(fabsf(v.y)));
+    m = max(m, __float_as_uint(fabsf(v.z)));
+    m = max(m, __float_as_uint(fabsf(v.w)));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(amax_bits + e, m);
+}
+
+__global__ void finalize_g_kernel(uint32_t *bits, int E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const float amax = __uint_as_float(bits[e]);
+  const float g = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+  bits[e] = __float_as_uint(g);
+}
+
+// E4M3 code of x >= 0: nearest, ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (!(x > 0.0f)) return 0;
+  if (x >= 448.0f) return 0x7e;
+  int ex;
+  frexpf(x, &ex);                       // x = f * 2^ex, f in [0.5, 1)
+  const int e = max(ex - 1, -6);        // floor(log2 x), subnormal range below 2^-6
+  const float q = rintf(ldexpf(x, 3 - e));   // 3 fraction bits, exact scaling
+  const int code = (e + 7) * 8 + (int)q - 8; // continuous across binades
+  return (uint32_t)min(code, 0x7e);
+}
+
+// E2M1 code: nearest magnitude of {0,.5,1,1.5,2,3,4,6}, ties to even,
+// saturating at 6; a zero magnitude is +0.
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  const float a = fabsf(q);
+  uint32_t c;
+  if (!(a < 6.0f)) {
+    c = 7;
+  } else if (a < 1.0f) {
+    c = (uint32_t)rintf(a * 2.0f);                  // 0, 1 or 2
+  } else {
+    int ex;
+    frexpf(a, &ex);
+    const int e = ex - 1;                           // 0, 1 or 2
+    const float m = rintf(ldexpf(a, 1 - e));        // 2, 3 or 4
+    c = (uint32_t)((e + 1) * 2 + (int)m - 2);
+  }
+  if (q < 0.0f && c) c |= 8u;
+  return c;
+}
+
+__global__ __launch_bounds__(PACK_THREADS) void quantize_kernel(
+    const float4 *__restrict__ dense, long long total_groups, long long groups_per_expert,
+    const float *__restrict__ gscale, uint16_t *__restrict__ values, uint8_t *__restrict__ masks,
+    uint8_t *__restrict__ scales) {
+  const long long G = (long long)blockIdx.x * PACK_THREADS + threadIdx.x;
+  const bool valid = G < total_groups;
+  float w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float g = 1.0f;
+  if (valid) {
+    const float4 lo = dense[2 * G], hi = dense[2 * G + 1];
+    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+    w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+    g = gscale[G / groups_per_expert];
+  }
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = fabsf(w[i]);
+  // support: position i is kept iff fewer than 4 positions beat it
+  uint32_t mask = 0;
+  float gmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int beat = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) beat += (a[j] > a[i]) || (a[j] == a[i] && j < i);
+    if (beat < 4) mask |= 1u << i;
+    gmax = fmaxf(gmax, a[i]);
+  }
+  // block maximum over the 4 groups of this 32-weight block
+  float bmax = fmaxf(gmax, __shfl_xor(gmax, 1, 64));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 2, 64));
+  const float six_g = 6.0f * g;
+  const uint32_t sc = e4m3_encode(__fdiv_rn(bmax, six_g));
+  const float sg = e4m3_to_f32(sc) * g;
+  uint32_t codes = 0;
+  int j = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if ((mask >> i) & 1u) {
+      const float q = sg > 0.0f ? __fdiv_rn(w[i], sg) : 0.0f;
+      codes |= e2m1_encode(q) << (4 * j);
+      ++j;
+    }
+  }
+  if (valid) {
+    values[G] = (uint16_t)codes;
+    masks[G] = (uint8_t)mask;
+    if ((G & 3) == 0) scales[G >> 2] = (uint8_t)sc;
+  }
+}
+
+// dense[n][8g .. 8g+8) = decoded group g of row n of one expert (bf16, no
+// global scale).
+__global__ __launch_bounds__(PACK_THREADS) void decode_kernel(
+    const uint16_t *__restrict__ values, const uint8_t *__restrict__ masks,
+    const uint8_t *__restrict__ scales, long long groups, uint4 *__restrict__ dense) {
+  __shared__ uint4 lut[256];
+  build_group_lut(lut);
+  __syncthreads();
+  const long long G = (long long)blockIdx.x * PACK_THREADS + threadIdx.x;
+  if (G >= groups) return;
+  const uint32_t v = values[G];
+  const float s = e4m3_to_f32(scales[G >> 2]);
+  dense[G] = decode_group<0>(masks[G], v, s, lut);
+}
+
+}  // namespace moesq
+
+using namespace moesq;
+
+extern "C" moesq_status_t moesq_pack_weights(const float *dense, int32_t E, int32_t N, int32_t K,
+                                             uint8_t *values, uint8_t *masks, uint8_t *scales,
+                                             float *global_scale, hipStream_t stream) {
+  clear_error();
+  if (E < 1 || E > 65535 || N < 1 || K < 32 || K % 32)
+    return fail(MOESQ_ERR_SHAPE,
+                "moesq_pack_weights: need 1 <= E <= 65535, N >= 1, K a positive multiple of 32");
+  if (!dense || !values || !masks || !scales || !global_scale)
+    return fail(MOESQ_ERR_NULL, "moesq_pack_weights: NULL pointer");
+  const long long per_expert = (long long)N * K;
+  uint32_t *bits = reinterpret_cast<uint32_t *>(global_scale);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, bits, E, 0u);
+  long long bx = (per_expert / 4 + PACK_THREADS * 16 - 1) / (PACK_THREADS * 16);
+  if (bx > 1024) bx = 1024;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)bx, E), dim3(PACK_THREADS), 0, stream,
+                     (const float4 *)dense, per_expert / 4, bits);
+  hipLaunchKernelGGL(finalize_g_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, bits, E);
+  const long long groups = (long long)E * per_expert / 8;
+  const long long blocks = (groups + PACK_THREADS - 1) / PACK_THREADS;
+  if (blocks >= (1ll << 31)) return fail(MOESQ_ERR_SHAPE, "moesq_pack_weights: too many groups");
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, stream,
+                     (const float4 *)dense, groups, per_expert / 8, global_scale,
+                     (uint16_t *)values, masks, scales);
+  return launch_status("moesq_pack_weights");
+}
+
+extern "C" moesq_status_t moesq_decode_weights(const moesq_weights_t *w, int32_t expert,
+                                               uint16_t *dense, hipStream_t stream) {
+  clear_error();
+  if (!w || !dense) return fail(MOESQ_ERR_NULL, "moesq_decode_weights: NULL pointer");
+  if (w->layout != MOESQ_LAYOUT_CANONICAL)
+    return fail(MOESQ_ERR_LAYOUT, "moesq_decode_weights: unknown layout");
+  if (!w->values || !w->masks || !w->scales)
+    return fail(MOESQ_ERR_NULL, "moesq_decode_weights: NULL weight buffer");
+  if (w->E < 1 || w->N < 1 || w->K < 32 || w->K % 32)
+    return fail(MOESQ_ERR_SHAPE, "moesq_decode_weights: bad E/N/K");
+  if (expert < 0 || expert >= w->E)
+    return fail(MOESQ_ERR_ARG, "moesq_decode_weights: expert out of range");
+  const long long groups = (long long)w->N * w->K / 8;
+  const long long g0 = (long long)expert * groups;
+  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)((groups + PACK_THREADS - 1) / PACK_THREADS)),
+                     dim3(PACK_THREADS), 0, stream, (const uint16_t *)w->values + g0,
+                     w->masks + g0, w->scales + g0 / 4, groups, (uint4 *)dense);
+  return launch_status("moesq_decode_weights");
+}

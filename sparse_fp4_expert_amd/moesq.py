@@ -1,0 +1,239 @@
+"""Python binding of libmoesq (ctypes).
+
+Argument marshalling only: every function here checks tensor placement,
+dtype and contiguity, passes raw device pointers and the current HIP stream
+to the C ABI in include/moesq.h, and raises MoesqError on a non-zero status.
+All compute runs in the library's HIP kernels.  Torch supplies device memory
+and streams; the convenience helpers at the bottom allocate outputs with
+torch and call the same entry points.
+
+The library must be built first (python -m sparse_fp4_expert_amd.build);
+importing this module without it raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoesq.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m sparse_fp4_expert_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_LAYOUT, ERR_HIP, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
+EPI_NONE, EPI_SWIGLU = 0, 1
+LAYOUT_CANONICAL = 0
+MAX_EXPERTS = 1024
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+class WeightsDesc(ctypes.Structure):
+    """moesq_weights_t."""
+    _fields_ = [("values", _vp), ("masks", _vp), ("scales", _vp), ("global_scale", _vp),
+                ("E", _i32), ("N", _i32), ("K", _i32), ("layout", _i32)]
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_route = _sig("moesq_route", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp)
+_route_ws = _sig("moesq_route_workspace_bytes", _sz, _i32, _i32, _i32)
+_permute = _sig("moesq_permute", _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
+_spgemm = _sig("moesq_grouped_spgemm", _i32, _vp, _vp, _i32, ctypes.POINTER(WeightsDesc), _i32,
+               _vp, _vp, _sz, _vp)
+_spgemm_ws = _sig("moesq_spgemm_workspace_bytes", _sz, _i32, ctypes.POINTER(WeightsDesc))
+_unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
+_pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
+_decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
+_status_string = _sig("moesq_status_string", ctypes.c_char_p, _i32)
+_last_error = _sig("moesq_last_error", ctypes.c_char_p)
+_version = _sig("moesq_version", _i32)
+
+EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
+            "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes", "moesq_unpermute",
+            "moesq_pack_weights", "moesq_decode_weights", "moesq_status_string",
+            "moesq_last_error", "moesq_version"]
+
+
+class MoesqError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_string(status).decode()} ({detail})")
+
+
+def _check(st: int):
+    if st != OK:
+        raise MoesqError(st, _last_error().decode())
+
+
+def version() -> int:
+    return _version()
+
+
+def _ptr(t, dtype, name, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Weights:
+    """Device tensors of compressed experts in the canonical layout.
+
+    values uint8 [E, N, K/4], masks uint8 [E, N, K/8], scales uint8 [E, N, K/32],
+    global_scale float32 [E]."""
+
+    def __init__(self, values, masks, scales, global_scale):
+        E, N, K4 = values.shape
+        self.E, self.N, self.K = int(E), int(N), int(K4) * 4
+        for t, shape, name in [(masks, (E, N, self.K // 8), "masks"),
+                               (scales, (E, N, self.K // 32), "scales"),
+                               (global_scale, (E,), "global_scale")]:
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        self.values, self.masks, self.scales, self.global_scale = values, masks, scales, global_scale
+        self.desc = WeightsDesc(_ptr(values, torch.uint8, "values"), _ptr(masks, torch.uint8, "masks"),
+                                _ptr(scales, torch.uint8, "scales"),
+                                _ptr(global_scale, torch.float32, "global_scale"),
+                                self.E, self.N, self.K, LAYOUT_CANONICAL)
+
+    @property
+    def nbytes(self) -> int:
+        return self.values.numel() + self.masks.numel() + self.scales.numel() + 4 * self.E
+
+    def expert_nbytes(self) -> int:
+        return self.N * self.K * 13 // 32 + 4
+
+    @staticmethod
+    def empty(E: int, N: int, K: int, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        return Weights(torch.empty(E, N, K // 4, **u8), torch.empty(E, N, K // 8, **u8),
+                       torch.empty(E, N, K // 32, **u8),
+                       torch.empty(E, dtype=torch.float32, device=device))
+
+
+# ------------------------------------------------------------ C-ABI mirrors
+
+def moesq_route(topk_ids, T: int, k: int, E: int, expert_offsets, perm, inv_perm,
+                ws=None, stream=None):
+    _check(_route(_ptr(topk_ids, torch.int32, "topk_ids"), T, k, E,
+                  _ptr(expert_offsets, torch.int32, "expert_offsets"),
+                  _ptr(perm, torch.int32, "perm"), _ptr(inv_perm, torch.int32, "inv_perm"),
+                  _ptr(ws, torch.uint8, "ws", True), 0 if ws is None else ws.numel(),
+                  _stream(stream)))
+
+
+def moesq_route_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(_route_ws(T, k, E))
+
+
+def moesq_permute(x, perm, T: int, k: int, K: int, x_routed, stream=None):
+    _check(_permute(_ptr(x, torch.bfloat16, "x"), _ptr(perm, torch.int32, "perm"), T, k, K,
+                    _ptr(x_routed, torch.bfloat16, "x_routed"), _stream(stream)))
+
+
+def moesq_grouped_spgemm(x_routed, expert_offsets, M: int, w: Weights, epilogue: int, y,
+                         ws=None, stream=None):
+    _check(_spgemm(_ptr(x_routed, torch.bfloat16, "x_routed"),
+                   _ptr(expert_offsets, torch.int32, "expert_offsets"), M,
+                   ctypes.byref(w.desc), epilogue, _ptr(y, torch.bfloat16, "y"),
+                   _ptr(ws, torch.uint8, "ws", True), 0 if ws is None else ws.numel(),
+                   _stream(stream)))
+
+
+def moesq_spgemm_workspace_bytes(M: int, w: Weights) -> int:
+    return int(_spgemm_ws(M, ctypes.byref(w.desc)))
+
+
+def moesq_unpermute(y, inv_perm, topk_weights, T: int, k: int, N: int, out, stream=None):
+    _check(_unpermute(_ptr(y, torch.bfloat16, "y"), _ptr(inv_perm, torch.int32, "inv_perm"),
+                      _ptr(topk_weights, torch.float32, "topk_weights", True), T, k, N,
+                      _ptr(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, global_scale,
+                       stream=None):
+    _check(_pack(_ptr(dense, torch.float32, "dense"), E, N, K, _ptr(values, torch.uint8, "values"),
+                 _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
+                 _ptr(global_scale, torch.float32, "global_scale"), _stream(stream)))
+
+
+def moesq_decode_weights(w: Weights, expert: int, dense, stream=None):
+    _check(_decode(ctypes.byref(w.desc), expert, _ptr(dense, torch.bfloat16, "dense"),
+                   _stream(stream)))
+
+
+# ------------------------------------------------------------ helpers (allocate with torch)
+
+def route(topk_ids, E: int, k: int, stream=None):
+    """Returns (expert_offsets [E+1], perm [M], inv_perm [M]) as int32 device tensors."""
+    M = topk_ids.numel()
+    dev = topk_ids.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(M, dtype=torch.int32, device=dev)
+    inv = torch.empty(M, dtype=torch.int32, device=dev)
+    moesq_route(topk_ids, M // k, k, E, off, perm, inv, None, stream)
+    return off, perm, inv
+
+
+def permute(x, perm, k: int, stream=None):
+    T, K = x.shape
+    out = torch.empty(T * k, K, dtype=torch.bfloat16, device=x.device)
+    moesq_permute(x, perm, T, k, K, out, stream)
+    return out
+
+
+def grouped_spgemm(x_routed, expert_offsets, w: Weights, epilogue: int = EPI_NONE, out=None,
+                   stream=None):
+    M = x_routed.shape[0]
+    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    if out is None:
+        out = torch.empty(M, n_out, dtype=torch.bfloat16, device=x_routed.device)
+    moesq_grouped_spgemm(x_routed, expert_offsets, M, w, epilogue, out, None, stream)
+    return out
+
+
+def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):
+    N = y.shape[1]
+    rows = T if topk_weights is not None else T * k
+    out = torch.empty(rows, N, dtype=torch.bfloat16, device=y.device)
+    moesq_unpermute(y, inv_perm, topk_weights, T, k, N, out, stream)
+    return out
+
+
+def pack_weights(dense, stream=None) -> Weights:
+    """dense float32 [E, N, K] on the GPU -> Weights."""
+    E, N, K = dense.shape
+    w = Weights.empty(E, N, K, device=dense.device)
+    moesq_pack_weights(dense, E, N, K, w.values, w.masks, w.scales, w.global_scale, stream)
+    return w
+
+
+def decode_weights(w: Weights, expert: int, stream=None):
+    out = torch.empty(w.N, w.K, dtype=torch.bfloat16, device=w.values.device)
+    moesq_decode_weights(w, expert, out, stream)
+    return out

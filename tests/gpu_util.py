@@ -1,0 +1,60 @@
+"""Helpers of the GPU parity tests: tolerance check, building a workload's
+inputs on the GPU, and oracle references for sampled experts."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+# Tolerance of the bf16 outputs against the float64 oracle, per tensor:
+# relative Frobenius error and max abs error relative to max |ref|.
+REL_FRO = 5e-3
+MAX_ABS_REL = 1e-2
+
+
+def tol_check(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / nref if nref > 0 else np.linalg.norm(got)
+    mx = np.abs(got - ref).max() if got.size else 0.0
+    lim = MAX_ABS_REL * (np.abs(ref).max() if ref.size else 0.0)
+    assert rel <= REL_FRO, f"{what}: relative Frobenius error {rel:.3e} > {REL_FRO}"
+    assert mx <= lim, f"{what}: max abs error {mx:.3e} > {lim:.3e}"
+    return rel, mx
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def pack_workload(m, wl, proj: int, chunk: int = 16):
+    """Dense weights of every expert drawn on the GPU and packed there, a
+    chunk of experts at a time.  Returns the library's Weights."""
+    _, N, K = wl.proj[proj]
+    w = m.Weights.empty(wl.E, N, K)
+    for c0 in range(0, wl.E, chunk):
+        c1 = min(wl.E, c0 + chunk)
+        dense = synth.dense_experts(wl, proj, range(c0, c1), device="cuda")
+        m.moesq_pack_weights(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1],
+                             w.scales[c0:c1], w.global_scale[c0:c1])
+        del dense
+    return w
+
+
+def oracle_expert(wl, proj: int, e: int, device="cuda"):
+    """The oracle's compression of the same dense weights (drawn on `device`
+    exactly as pack_workload draws them, then moved to the CPU)."""
+    dense = synth.dense_expert(wl, proj, e, device=device).cpu().numpy()
+    return oracle.quantize(dense)
+
+
+def assert_same_pack(w, e: int, p: oracle.PackedExpert, what=""):
+    assert np.array_equal(w.values[e].cpu().numpy(), p.values), f"{what}: values differ"
+    assert np.array_equal(w.masks[e].cpu().numpy(), p.masks), f"{what}: masks differ"
+    assert np.array_equal(w.scales[e].cpu().numpy(), p.scales), f"{what}: scales differ"
+    assert w.global_scale[e].item() == float(p.g), f"{what}: global scale differs"

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every symbol include/moesq.h declares, and
+rejects bad arguments on the host before touching the GPU.  No GPU: only
+argument checks that return before any HIP call are exercised."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moesq.h")
+LIB = os.path.join(ROOT, "sparse_fp4_expert_amd", "libmoesq.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moesq_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoesq.so is not built: run python -m sparse_fp4_expert_amd.build")
+    return ctypes.CDLL(LIB)
+
+
+@pytest.fixture(scope="module")
+def m():
+    from sparse_fp4_expert_amd import moesq
+    return moesq
+
+
+def test_exports_every_declared_symbol(lib, m):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(m.EXPORTED) == names
+
+
+def test_status_strings_and_version(m):
+    assert m.version() >= 100
+    for st in [m.OK, m.ERR_NULL, m.ERR_SHAPE, m.ERR_WORKSPACE, m.ERR_LAYOUT, m.ERR_HIP, m.ERR_ARG]:
+        assert m._status_string(st).decode().startswith("MOESQ_")
+    assert m._route_ws(64, 2, 8) == 0
+
+
+def _desc(m, E=8, N=128, K=256, layout=0, null=False):
+    p = None if null else 0x1000
+    return m.WeightsDesc(p, p, p, p, E, N, K, layout)
+
+
+def test_route_rejects(m):
+    r = m._route
+    assert r(None, 4, 2, 0, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_SHAPE      # E = 0
+    assert r(None, 4, 2, 2000, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_SHAPE   # E too large
+    assert r(None, 4, 9, 8, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_SHAPE      # k > E
+    assert r(None, -1, 2, 8, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_SHAPE     # T < 0
+    assert r(None, 4, 2, 8, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_NULL       # ids NULL
+    assert r(0x10, 4, 2, 8, None, 0x10, 0x10, None, 0, None) == m.ERR_NULL
+    assert b"expert_offsets" in m._last_error()
+    assert r(0x10, 1 << 30, 4, 8, 0x10, 0x10, 0x10, None, 0, None) == m.ERR_SHAPE  # T*k >= 2^31
+    assert b"2^31" in m._last_error()
+
+
+def test_permute_unpermute_reject(m):
+    assert m._permute(0x10, 0x10, 4, 2, 12, 0x10, None) == m.ERR_SHAPE            # K % 8
+    assert m._permute(None, 0x10, 4, 2, 16, 0x10, None) == m.ERR_NULL
+    assert m._permute(None, None, 0, 2, 16, None, None) == m.OK                   # empty: no-op
+    assert m._unpermute(0x10, 0x10, None, 4, 2, 12, 0x10, None) == m.ERR_SHAPE     # N % 8
+    assert m._unpermute(0x10, None, None, 4, 2, 16, 0x10, None) == m.ERR_NULL
+    assert m._unpermute(0x10, 0x10, None, 4, 0, 16, 0x10, None) == m.ERR_SHAPE     # k < 1
+
+
+def test_spgemm_rejects(m):
+    ref = ctypes.byref
+    g = m._spgemm
+    ok_off = 0x10
+    assert g(0x10, ok_off, 4, None, 0, 0x10, None, 0, None) == m.ERR_NULL
+    assert g(0x10, ok_off, 4, ref(_desc(m, layout=7)), 0, 0x10, None, 0, None) == m.ERR_LAYOUT
+    assert g(0x10, ok_off, 4, ref(_desc(m, null=True)), 0, 0x10, None, 0, None) == m.ERR_NULL
+    assert g(0x10, ok_off, 4, ref(_desc(m, K=48)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
+    assert g(0x10, ok_off, 4, ref(_desc(m, N=24)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
+    assert g(0x10, ok_off, 4, ref(_desc(m, E=0)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
+    assert g(0x10, ok_off, 4, ref(_desc(m, E=1025)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
+    assert g(0x10, ok_off, 4, ref(_desc(m, N=48)), 1, 0x10, None, 0, None) == m.ERR_SHAPE  # SwiGLU N%32
+    assert g(0x10, ok_off, 4, ref(_desc(m)), 5, 0x10, None, 0, None) == m.ERR_ARG          # epilogue
+    assert g(0x10, None, 4, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_NULL
+    assert g(0x10, ok_off, -1, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
+    assert g(None, ok_off, 0, ref(_desc(m)), 0, None, None, 0, None) == m.OK                # M = 0
+    assert g(None, ok_off, 4, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_NULL
+
+
+def test_pack_and_decode_reject(m):
+    assert m._pack(0x10, 1, 16, 48, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE
+    assert m._pack(0x10, 0, 16, 64, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE
+    assert m._pack(None, 1, 16, 64, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_NULL
+    d = _desc(m)
+    assert m._decode(ctypes.byref(d), 8, 0x10, None) == m.ERR_ARG
+    assert m._decode(ctypes.byref(d), -1, 0x10, None) == m.ERR_ARG
+    assert m._decode(ctypes.byref(d), 0, None, None) == m.ERR_NULL
+    assert m._decode(None, 0, 0x10, None) == m.ERR_NULL

@@ -1,0 +1,322 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the
+same seeded inputs.  Integer and byte results are bit-exact; bf16 outputs
+meet the relative-Frobenius / max-abs tolerance of gpu_util.tol_check.
+
+Run on an MI355X: python -u -m pytest tests -m gpu -x -v"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_same_pack, f64, oracle_expert, pack_workload, tol_check)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _route_ref(ids, E):
+    return oracle.route(ids, E)
+
+
+def _gpu_route(m, ids_np, E, k):
+    ids = torch.from_numpy(ids_np).cuda()
+    off, perm, inv = m.route(ids, E, k)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy()
+
+
+def _pick(counts, rng, n_random=2):
+    """Experts to sample: the largest, a tiny one (< 16 rows), a mid one, and
+    a few random active experts."""
+    active = np.nonzero(counts)[0]
+    pick = {int(active[np.argmax(counts[active])])}
+    small = active[counts[active] < 16]
+    if len(small):
+        pick.add(int(small[0]))
+    mid = active[(counts[active] >= 16) & (counts[active] <= 200)]
+    if len(mid):
+        pick.add(int(mid[len(mid) // 2]))
+    for e in rng.choice(active, size=min(n_random, len(active)), replace=False):
+        pick.add(int(e))
+    return sorted(pick)
+
+
+# ------------------------------------------------------------------ packing
+
+def test_pack_golden_rows(lib):
+    """The GPU packer reproduces the hand-derived fixture bytes."""
+    import pins
+    d = {ln[0]: ln[1:] for ln in pins._lines("quant_rows.txt")}
+    W = torch.tensor([[float(v) for v in d["w0"]], [float(v) for v in d["w1"]]],
+                     dtype=torch.float32).reshape(1, 2, 64).cuda()
+    w = lib.pack_weights(W)
+    torch.cuda.synchronize()
+    for r in range(2):
+        assert w.masks[0, r].cpu().numpy().tolist() == [int(t, 16) for t in d[f"masks{r}"]]
+        assert w.values[0, r].cpu().numpy().tolist() == [int(t, 16) for t in d[f"values{r}"]]
+        assert w.scales[0, r].cpu().numpy().tolist() == [int(t, 16) for t in d[f"scales{r}"]]
+    assert w.global_scale[0].item() == float(d["g"][0])
+
+
+def test_pack_and_decode_tiny(lib):
+    wl = synth.WORKLOADS["tiny"]
+    dense = synth.dense_experts(wl, 0)                      # CPU draw, same tensor both sides
+    w = lib.pack_weights(dense.cuda())
+    torch.cuda.synchronize()
+    for e in range(wl.E):
+        p = oracle.quantize(dense[e].numpy())
+        assert_same_pack(w, e, p, f"expert {e}")
+        dec = lib.decode_weights(w, e)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(dec), oracle.decode(p, include_global=False)), e
+
+
+def test_pack_extreme_ranges(lib):
+    """Subnormal and zero block scales, saturating values, ties, all-zero rows
+    and an all-zero expert."""
+    g = torch.Generator().manual_seed(11)
+    E, N, K = 3, 32, 256
+    d = torch.randn(E, N, K, generator=g)
+    d[0] *= torch.pow(10.0, torch.empty(N, 1).uniform_(-9, 1, generator=g))   # per-row range
+    d[0, 3] = 0.0                                                            # zero row
+    d[0, 4, :64] = 0.25                                                      # all-equal groups
+    d[1, :, ::7] *= 300.0                                                    # strong outliers
+    d[2] = 0.0                                                               # zero expert
+    w = lib.pack_weights(d.cuda())
+    torch.cuda.synchronize()
+    for e in range(E):
+        p = oracle.quantize(d[e].numpy())
+        assert_same_pack(w, e, p, f"expert {e}")
+        assert np.array_equal(f64(lib.decode_weights(w, e)), oracle.decode(p, include_global=False))
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_route_workloads(lib, name):
+    wl = synth.WORKLOADS[name]
+    ids, _ = synth.routing(wl)
+    got = _gpu_route(lib, ids, wl.E, wl.k)
+    ref = _route_ref(ids, wl.E)
+    for a, b, what in zip(got, ref, ["offsets", "perm", "inv_perm"]):
+        assert np.array_equal(a, b), f"{name}: {what} differs"
+
+
+@pytest.mark.parametrize("E,M,k,mode", [
+    (1, 64, 1, "random"), (8, 1, 1, "random"), (8, 640, 4, "same"), (1024, 70000, 2, "random"),
+    (384, 65536, 8, "skew"), (5, 63, 3, "random"), (2, 129, 1, "random")])
+def test_route_edges(lib, E, M, k, mode):
+    rng = np.random.default_rng(E * 7 + M)
+    if mode == "same":
+        ids = np.full(M, E - 1, np.int32)
+    elif mode == "skew":
+        ids = np.minimum(rng.zipf(1.3, M) - 1, E - 1).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, M).astype(np.int32)
+    got = _gpu_route(lib, ids, E, k)
+    ref = _route_ref(ids, E)
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
+
+
+def test_route_invalid_ids(lib):
+    E, k = 6, 2
+    ids = np.array([0, 5, -1, 3, 6, 3, 1000, 0, 2, 5], np.int32)
+    off, perm, inv = _gpu_route(lib, ids, E, k)
+    valid = (ids >= 0) & (ids < E)
+    vidx = np.nonzero(valid)[0]
+    o2, p2, _ = oracle.route(ids[valid], E)
+    assert np.array_equal(off, o2)
+    n = len(vidx)
+    assert np.array_equal(perm[:n], vidx[p2])
+    assert (inv[~valid] == -1).all()
+    assert np.array_equal(inv[vidx[p2]], np.arange(n))
+
+
+# ------------------------------------------------------------------ dispatch and combine
+
+@pytest.mark.parametrize("name", ["tiny", "decode-1t", "prefill-30b"])
+def test_permute(lib, name):
+    wl = synth.WORKLOADS[name]
+    ids, _ = synth.routing(wl)
+    x = synth.tokens(wl)
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    xr = lib.permute(x.cuda(), perm, wl.k)
+    torch.cuda.synchronize()
+    _, pref, _ = oracle.route(ids, wl.E)
+    assert torch.equal(xr.cpu(), x[torch.from_numpy(pref.astype(np.int64)) // wl.k])
+
+
+@pytest.mark.parametrize("T,k,N", [(64, 2, 128), (1024, 8, 7168), (5, 3, 8)])
+def test_unpermute(lib, T, k, N):
+    E = max(k, 16)
+    rng = np.random.default_rng(T + N)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).reshape(-1).astype(np.int32)
+    w = rng.random(T * k).astype(np.float32)
+    g = torch.Generator().manual_seed(T * N)
+    y = torch.randn(T * k, N, generator=g).to(torch.bfloat16)
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), E, k)
+    yd = y.cuda()
+    out_w = lib.unpermute(yd, inv, torch.from_numpy(w).cuda(), T, k)
+    out_f = lib.unpermute(yd, inv, None, T, k)
+    torch.cuda.synchronize()
+    _, _, inv_ref = oracle.route(ids, E)
+    y64 = y.to(torch.float64).numpy()
+    tol_check(f64(out_w), oracle.unpermute(y64, inv_ref, w, T, k), "weighted combine")
+    assert np.array_equal(f64(out_f), oracle.unpermute(y64, inv_ref, None, T, k))
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def _full_oracle_gemm(ids, E, k, x, packs, swiglu=False, packs2=None, weights=None):
+    off, perm, inv = oracle.route(ids, E)
+    dec = [oracle.decode(p) for p in packs]
+    xr = oracle.permute(x.to(torch.float64).numpy(), perm, k)
+    y = oracle.grouped_gemm(xr, off, lambda e: dec[e])
+    return off, perm, inv, y
+
+
+def test_spgemm_tiny_end_to_end(lib):
+    """tiny: route -> permute -> GEMM -> flat and weighted combine, every
+    output against the oracle."""
+    wl = synth.WORKLOADS["tiny"]
+    ids, tw = synth.routing(wl)
+    x = synth.tokens(wl)
+    dense = synth.dense_experts(wl, 0)
+    packs = [oracle.quantize(dense[e].numpy()) for e in range(wl.E)]
+    w = lib.pack_weights(dense.cuda())
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    xr = lib.permute(x.cuda(), perm, wl.k)
+    y = lib.grouped_spgemm(xr, off, w)
+    out = lib.unpermute(y, inv, torch.from_numpy(tw).cuda(), wl.T, wl.k)
+    flat = lib.unpermute(y, inv, None, wl.T, wl.k)
+    torch.cuda.synchronize()
+    off_r, perm_r, inv_r, y_ref = _full_oracle_gemm(ids, wl.E, wl.k, x, packs)
+    tol_check(f64(y), y_ref, "Y")
+    tol_check(f64(flat), oracle.unpermute(y_ref, inv_r, None, wl.T, wl.k), "flat combine")
+    tol_check(f64(out), oracle.unpermute(y_ref, inv_r, tw, wl.T, wl.k), "weighted combine")
+
+
+def _edge_case(lib, loads, N, K, swiglu, seed):
+    E = len(loads)
+    ids = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(loads)])
+    rng = np.random.default_rng(seed)
+    ids = ids[rng.permutation(len(ids))]
+    M = len(ids)
+    wl = synth.Workload("edge", E=E, T=M, k=1, proj=(("w", N, K),), outliers=True,
+                        bias="none", seed=seed)
+    x = synth.tokens(wl, T=M, K=K)
+    dense = synth.dense_experts(wl, 0)
+    packs = [oracle.quantize(dense[e].numpy()) for e in range(E)]
+    w = lib.pack_weights(dense.cuda())
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), E, 1)
+    xr = lib.permute(x.cuda(), perm, 1)
+    y = lib.grouped_spgemm(xr, off, w, lib.EPI_SWIGLU if swiglu else lib.EPI_NONE)
+    torch.cuda.synchronize()
+    _, _, _, y_ref = _full_oracle_gemm(ids, E, 1, x, packs)
+    if swiglu:
+        y_ref = oracle.bf16_round(oracle.swiglu(y_ref))
+    tol_check(f64(y), y_ref, f"loads={loads} N={N} K={K} swiglu={swiglu}")
+
+
+@pytest.mark.parametrize("loads,N,K,swiglu", [
+    ([0, 1, 15, 16, 17, 33, 130, 0], 64, 96, False),
+    ([0, 1, 15, 16, 17, 33, 130, 0], 64, 96, True),
+    ([300], 48, 32, False),
+    ([0, 0, 0, 200, 0], 272, 160, False),
+    ([0, 0, 0, 200, 0], 288, 160, True),
+    ([5, 0, 64, 127, 128, 129, 1], 16, 416, False),
+    ([1] * 20, 128, 256, True),
+])
+def test_spgemm_edges(lib, loads, N, K, swiglu):
+    _edge_case(lib, loads, N, K, swiglu, seed=sum(loads) + N + K)
+
+
+@pytest.mark.parametrize("name", ["decode-30b", "prefill-30b"])
+def test_spgemm_30b_workloads(lib, name):
+    """Full-size 30B-class workloads; sampled experts are checked against the
+    oracle: their packed bytes and every routed row (up to 256 per expert)."""
+    wl = synth.WORKLOADS[name]
+    _, N, K = wl.proj[0]
+    ids, _ = synth.routing(wl)
+    x = synth.tokens(wl)
+    say(f"[{name}] packing {wl.E} experts on the GPU")
+    w = pack_workload(lib, wl, 0)
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    xr = lib.permute(x.cuda(), perm, wl.k)
+    say(f"[{name}] grouped GEMM M={wl.M} N={N} K={K}")
+    y = lib.grouped_spgemm(xr, off, w)
+    torch.cuda.synchronize()
+    off_r, perm_r, _ = oracle.route(ids, wl.E)
+    counts = np.diff(off_r)
+    x64 = x.to(torch.float64).numpy()
+    rng = np.random.default_rng(wl.seed)
+    for e in _pick(counts, rng):
+        p = oracle_expert(wl, 0, e)
+        assert_same_pack(w, e, p, f"{name} expert {e}")
+        rows = np.arange(off_r[e], off_r[e + 1])
+        if len(rows) > 256:
+            rows = np.concatenate([rows[:128], rows[-128:]])
+        ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], oracle.decode(p))
+        tol_check(f64(y[torch.from_numpy(rows).cuda()]), ref, f"{name} expert {e} ({counts[e]} rows)")
+        say(f"[{name}] expert {e}: {counts[e]} rows ok")
+
+
+@pytest.mark.parametrize("name", ["decode-1t", "prefill-1t"])
+def test_chain_1t_workloads(lib, name):
+    """Full-size trillion-class chain: permute -> gate/up GEMM with SwiGLU ->
+    down GEMM -> combine.  Sampled experts: packed bytes, h rows and Y2 rows
+    against the oracle chain; the weighted combine at full size against the
+    weighted sum of the device's own Y2 rows (a property that holds at any
+    size)."""
+    wl = synth.WORKLOADS[name]
+    ids, tw = synth.routing(wl)
+    x = synth.tokens(wl)
+    say(f"[{name}] packing 2 x {wl.E} experts on the GPU")
+    w1 = pack_workload(lib, wl, 0)
+    w2 = pack_workload(lib, wl, 1)
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    xr = lib.permute(x.cuda(), perm, wl.k)
+    say(f"[{name}] chain M={wl.M}")
+    h = lib.grouped_spgemm(xr, off, w1, lib.EPI_SWIGLU)
+    y2 = lib.grouped_spgemm(h, off, w2)
+    tw_d = torch.from_numpy(tw).cuda()
+    out = lib.unpermute(y2, inv, tw_d if wl.weighted_combine else None, wl.T, wl.k)
+    torch.cuda.synchronize()
+    off_r, perm_r, inv_r = oracle.route(ids, wl.E)
+    counts = np.diff(off_r)
+    x64 = x.to(torch.float64).numpy()
+    rng = np.random.default_rng(wl.seed)
+    for e in _pick(counts, rng, n_random=1):
+        p1 = oracle_expert(wl, 0, e)
+        p2 = oracle_expert(wl, 1, e)
+        assert_same_pack(w1, e, p1, f"{name} gate_up expert {e}")
+        assert_same_pack(w2, e, p2, f"{name} down expert {e}")
+        rows = np.arange(off_r[e], off_r[e + 1])
+        if len(rows) > 128:
+            rows = np.concatenate([rows[:64], rows[-64:]])
+        y1_ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], oracle.decode(p1))
+        h_ref = oracle.bf16_round(oracle.swiglu(y1_ref))
+        y2_ref = oracle.expert_gemm(h_ref, oracle.decode(p2))
+        rows_t = torch.from_numpy(rows).cuda()
+        tol_check(f64(h[rows_t]), h_ref, f"{name} h, expert {e}")
+        tol_check(f64(y2[rows_t]), y2_ref, f"{name} Y2, expert {e}")
+        say(f"[{name}] expert {e}: {counts[e]} rows ok")
+    if wl.weighted_combine:
+        # computed by torch in float64 on the device, from the device's own Y2
+        invr = torch.from_numpy(inv_r.reshape(wl.T, wl.k).astype(np.int64)).cuda()
+        twr = tw_d.reshape(wl.T, wl.k).double()
+        want = torch.zeros(wl.T, y2.shape[1], dtype=torch.float64, device="cuda")
+        for j in range(wl.k):
+            want += twr[:, j:j + 1] * y2[invr[:, j]].double()
+        tol_check(f64(out), f64(want), f"{name} weighted combine")
+    else:
+        assert torch.equal(out, y2[torch.from_numpy(inv_r.astype(np.int64)).cuda()])

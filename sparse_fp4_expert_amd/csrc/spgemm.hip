@@ -4,26 +4,29 @@
 // every routing-dependent expert problem within one launch, with the sparse
 // weights as the first MMA operand.  Here the weights stay compressed in HBM
 // (13/32 byte per logical weight) and are decoded in registers straight into
-// the A operand of v_mfma_f32_16x16x32_bf16: the decoded values E2M1*E4M3
-// are exact in bf16, so only the fp32 accumulation and the final bf16
-// rounding round.  Routed tokens are the B operand, staged through LDS.
+// the A operand of a bf16 MFMA (v_mfma_f32_16x16x32_bf16 or
+// v_mfma_f32_32x32x16_bf16): the decoded values E2M1*E4M3 are exact in bf16,
+// so only the fp32 accumulation and the final bf16 rounding round.  Routed
+// tokens are the B operand, staged through LDS by direct global->LDS loads.
 //
 // Work decomposition.  An item is (expert e, token tile of up to BM routed
 // rows, row tile of BN weight rows).  Every workgroup reads the expert
 // offsets into LDS, forms the per-expert item counts and their prefix, and
-// walks items blockIdx.x, blockIdx.x + gridDim.x, ...; so the grid never
-// depends on the routing, which only the device knows.  Token tiles are
-// trimmed to whole 16-row MFMA fragments, so an expert with few rows costs
-// few MFMAs and mostly streams its weights.
+// walks the items with a grid-sized stride, so the grid never depends on the
+// routing, which only the device knows.  Token tiles are trimmed to whole
+// MFMA fragments, so an expert with few rows costs few MFMAs and mostly
+// streams its weights.
 //
-// K order inside a chunk of KC = 128.  The contraction order is free as long
-// as both operands agree, so lane group q = lane/16 owns the 32 K positions
-// [k0 + 32q, k0 + 32q + 32): one scale block, four groups of 8, 8 value
-// bytes, 4 mask bytes and one scale byte, each a single load.  At k-step s
-// (0..3) the A fragment of a lane is group s of its block, which is exactly
-// the 8 consecutive bf16 the MFMA expects per lane, and the B fragment is the
-// same 8 K positions of the lane's token, read from LDS.
+// K order.  The contraction order is free as long as both operands agree.
+// An MFMA of shape MS x MS x (8*LG) gives lane group q = lane / MS (LG = 64/MS
+// groups) eight consecutive K positions.  Inside a chunk of KC positions,
+// lane group q owns the KQ = KC/LG positions [k0 + KQ*q, k0 + KQ*q + KQ):
+// whole scale blocks, so its values, masks and scales are one load each, and
+// k-step s hands it the 4:8 group s of that range -- exactly one decoded
+// group per lane -- while the B fragment holds the same 8 positions of the
+// lane's token.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -38,46 +41,187 @@ struct SpgemmArgs {
   const float *gscale;
   uint16_t *y;
   int M, E, N, K;
-  int swiglu;
   int row_tiles;
 };
 
-constexpr int KC = 128;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int WAVES, int RF, int TF>
-__global__ __launch_bounds__(WAVES * 64) void spgemm_kernel(SpgemmArgs a) {
-  constexpr int THREADS = WAVES * 64;
-  constexpr int BM = TF * 16;
-  constexpr int BN = WAVES * RF * 16;
-  constexpr int PITCH = KC + 8;  // bf16 elements per LDS token row (+16 B breaks bank aliasing)
+template <int MS>
+struct Mfma;
+template <>
+struct Mfma<16> {
+  using C = f32x4_t;
+  static constexpr int NC = 4;
+  static __device__ __forceinline__ C run(uint4 a, uint4 b, C c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<32> {
+  using C = f32x16_t;
+  static constexpr int NC = 16;
+  static __device__ __forceinline__ C run(uint4 a, uint4 b, C c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  }
+};
+
+// Compressed weights of one lane for one K chunk: for each of its RF
+// fragment rows, the KQ positions of its lane group.
+template <int RF, int KQ>
+struct WChunk {
+  static constexpr int VD = KQ / 16;   // value dwords (8 nibbles each)
+  static constexpr int MD = KQ / 32;   // mask dwords (4 groups each)
+  uint32_t v[RF][VD];
+  uint32_t m[RF][MD];
+  uint32_t s[RF];                      // KQ/32 scale bytes
+};
+
+// vb/mb/sb: the expert's value/mask/scale bases; fv/fm/fs: byte offsets of
+// each fragment's first row (uniform); vo/mo/so: this lane's offsets inside
+// a fragment (its row and lane group).  ok[f]: the lane's first scale block
+// lies inside K; two-block ranges load only the first block when `whole` is
+// false (K ends in the middle of the range).
+template <int RF, int KQ>
+__device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb,
+                                            const uint8_t *mb, const uint8_t *sb,
+                                            const uint32_t (&fv)[RF], const uint32_t (&fm)[RF],
+                                            const uint32_t (&fs)[RF], uint32_t vo, uint32_t mo,
+                                            uint32_t so, const bool (&ok)[RF], bool whole, int k0) {
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    if (KQ == 64 && ok[f] && !whole) {
+      const uint8_t *pv = vb + (fv[f] + vo + (k0 >> 2));
+      const uint8_t *pm = mb + (fm[f] + mo + (k0 >> 3));
+      const uint8_t *ps = sb + (fs[f] + so + (k0 >> 5));
+      const uint2 v = *reinterpret_cast<const uint2 *>(pv);
+      w.v[f][0] = v.x;
+      w.v[f][1] = v.y;
+#pragma unroll
+      for (int i = 2; i < WChunk<RF, KQ>::VD; ++i) w.v[f][i] = 0;
+      w.m[f][0] = *reinterpret_cast<const uint32_t *>(pm);
+#pragma unroll
+      for (int i = 1; i < WChunk<RF, KQ>::MD; ++i) w.m[f][i] = 0;
+      w.s[f] = *ps;
+    } else if (ok[f]) {
+      const uint8_t *pv = vb + (fv[f] + vo + (k0 >> 2));
+      const uint8_t *pm = mb + (fm[f] + mo + (k0 >> 3));
+      const uint8_t *ps = sb + (fs[f] + so + (k0 >> 5));
+      if constexpr (KQ == 32) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(pv);
+        w.v[f][0] = v.x;
+        w.v[f][1] = v.y;
+        w.m[f][0] = *reinterpret_cast<const uint32_t *>(pm);
+        w.s[f] = *ps;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4 *>(pv);
+        w.v[f][0] = v.x;
+        w.v[f][1] = v.y;
+        w.v[f][2] = v.z;
+        w.v[f][3] = v.w;
+        const uint2 m = *reinterpret_cast<const uint2 *>(pm);
+        w.m[f][0] = m.x;
+        w.m[f][1] = m.y;
+        w.s[f] = *reinterpret_cast<const uint16_t *>(ps);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < WChunk<RF, KQ>::VD; ++i) w.v[f][i] = 0;
+#pragma unroll
+      for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) w.m[f][i] = 0;
+      w.s[f] = 0;
+    }
+  }
+}
+
+template <int RF, int KQ>
+__device__ __forceinline__ void decode_step(uint4 (&A)[RF], const WChunk<RF, KQ> &w,
+                                            const float (&sf)[RF][KQ / 32], const uint4 *lut,
+                                            int s) {
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const uint32_t m8 = (w.m[f][s >> 2] >> (8 * (s & 3))) & 0xffu;
+    const uint32_t vw = w.v[f][s >> 1];
+    A[f] = (s & 1) ? decode_group<2>(m8, vw, sf[f][s >> 2], lut)
+                   : decode_group<0>(m8, vw, sf[f][s >> 2], lut);
+  }
+}
+
+// Decode + MFMA over one K chunk staged in `tk`: token T's 16-byte unit c of
+// the chunk sits at element T*KC + 8*(c ^ (T % UPR)), so the MS lanes of a
+// lane group read MS different columns.  The A fragments of k-step s+1 are
+// decoded while the MFMAs of step s run; a scheduling barrier per step
+// bounds the live registers to two steps.  FULL: all TF token fragments hold
+// routed rows.
+template <int MS, int RF, int TF, int KC, bool FULL>
+__device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
+                                          const uint16_t *tk, const WChunk<RF, KC * MS / 64> &w,
+                                          const uint4 *lut, int nft, int q, int rl) {
+  constexpr int KQ = KC * MS / 64;
+  constexpr int S = KQ / 8;
+  constexpr int UPR = KC / 8;
+  float sf[RF][KQ / 32];
+#pragma unroll
+  for (int f = 0; f < RF; ++f)
+#pragma unroll
+    for (int b = 0; b < KQ / 32; ++b) sf[f][b] = e4m3_to_f32((w.s[f] >> (8 * b)) & 0xffu);
+  const uint16_t *brow = tk + rl * KC;
+  const int cbase = (KQ / 8) * q;
+  uint4 A[2][RF];
+  decode_step<RF, KQ>(A[0], w, sf, lut, 0);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    uint4 B[TF];
+#pragma unroll
+    for (int t = 0; t < TF; ++t)
+      if (FULL || t < nft)
+        B[t] = *reinterpret_cast<const uint4 *>(
+            brow + t * MS * KC + (((cbase + s) ^ ((t * MS + rl) & (UPR - 1))) << 3));
+    if (s + 1 < S) decode_step<RF, KQ>(A[(s + 1) & 1], w, sf, lut, s + 1);
+#pragma unroll
+    for (int t = 0; t < TF; ++t)
+      if (FULL || t < nft)
+#pragma unroll
+        for (int f = 0; f < RF; ++f) acc[f][t] = Mfma<MS>::run(A[s & 1][f], B[t], acc[f][t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void spgemm_kernel(
+    SpgemmArgs a) {
+  using MF = Mfma<MS>;
+  constexpr int LG = 64 / MS;          // lane groups
+  constexpr int BM = TF * MS;          // tokens per tile
+  constexpr int BN = WAVES * RF * MS;  // weight rows per tile
+  constexpr int KQ = KC / LG;          // K positions per lane group per chunk
+  constexpr int UPR = KC / 8;          // 16-byte units per token row of a chunk
+  constexpr int NBLK = BM * KC * 2 / 1024;  // 1 KB direct-to-LDS loads per chunk
+  constexpr int BPW = NBLK / WAVES;    // ... per wave
+  static_assert(NBLK % WAVES == 0, "token tile must split evenly over the waves");
+  static_assert(64 % UPR == 0, "a 1 KB load covers whole token rows");
   static_assert(RF % 2 == 0, "SwiGLU pairs gate and up fragments");
+  static_assert(KQ == 32 || KQ == 64, "a lane group covers one or two scale blocks");
 
   __shared__ uint4 lut[256];
   __shared__ int s_lo[MOESQ_MAX_EXPERTS + 1];
   __shared__ int s_item[MOESQ_MAX_EXPERTS + 1];
-  __shared__ __attribute__((aligned(16))) uint16_t tok[BM * PITCH];
+  __shared__ __attribute__((aligned(1024))) uint16_t tok[2][BM * KC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.E, N = a.N, K = a.K, M = a.M;
 
   build_group_lut(lut);
-  // clamped expert ranges: rows [s_lo[e], s_lo[e+1]) with 0 <= lo <= hi <= M
-  for (int e = tid; e <= E; e += THREADS) {
-    int o = a.offsets[e];
-    s_lo[e] = min(max(o, 0), M);
-  }
+  for (int e = tid; e <= E; e += WAVES * 64) s_lo[e] = min(max(a.offsets[e], 0), M);
   __syncthreads();
   if (wave == 0) {
-    // items per expert, exclusive prefix by one wave
+    // items per expert and their exclusive prefix, by one wave
     const int per = (E + 63) / 64;
     const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
     int sum = 0;
-    for (int e = e0; e < e1; ++e) {
-      const int rows = max(0, s_lo[e + 1] - s_lo[e]);
-      sum += (rows + BM - 1) / BM * a.row_tiles;
-    }
+    for (int e = e0; e < e1; ++e) sum += (max(0, s_lo[e + 1] - s_lo[e]) + BM - 1) / BM;
     int incl = sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -86,22 +230,32 @@ __global__ __launch_bounds__(WAVES * 64) void spgemm_kernel(SpgemmArgs a) {
     }
     int run = incl - sum;
     for (int e = e0; e < e1; ++e) {
-      s_item[e] = run;
-      const int rows = max(0, s_lo[e + 1] - s_lo[e]);
-      run += (rows + BM - 1) / BM * a.row_tiles;
+      s_item[e] = run * a.row_tiles;
+      run += (max(0, s_lo[e + 1] - s_lo[e]) + BM - 1) / BM;
     }
-    if (lane == 63) s_item[E] = incl;
+    if (lane == 63) s_item[E] = incl * a.row_tiles;
   }
   __syncthreads();
   const int total = s_item[E];
 
-  const int q = lane >> 4;      // lane group: K block inside the chunk
-  const int r16 = lane & 15;    // row inside an A fragment / token inside a B fragment
+  const int q = lane / MS;     // lane group: K range [k0 + KQ*q, +KQ) of a chunk
+  const int rl = lane % MS;    // A-fragment row / B-fragment token of this lane
   const int half = N >> 1;
   const size_t vrow = (size_t)(K >> 2), mrow = (size_t)(K >> 3), srow = (size_t)(K >> 5);
+  const int nk = (K + KC - 1) / KC;
+  const uint32_t vo = (uint32_t)rl * (uint32_t)vrow + (KQ / 4) * q;
+  const uint32_t mo = (uint32_t)rl * (uint32_t)mrow + (KQ / 8) * q;
+  const uint32_t so = (uint32_t)rl * (uint32_t)srow + (KQ / 32) * q;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // expert of this item: the largest e with s_item[e] <= item
+  // Items of one round of workgroups are spread XCD-major: the grid is a
+  // multiple of 8 and workgroup b runs on XCD b % 8, so consecutive items
+  // (the row tiles of one token tile) share that XCD's L2.
+  const int G = gridDim.x;
+  const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+
+  for (int base = 0; base < total; base += G) {
+    const int item = base + slot;
+    if (item >= total) break;
     int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -113,134 +267,185 @@ __global__ __launch_bounds__(WAVES * 64) void spgemm_kernel(SpgemmArgs a) {
     const int e_lo = s_lo[e], e_hi = max(e_lo, s_lo[e + 1]);
     const int tok0 = e_lo + tt * BM;
     const int ntok = min(BM, e_hi - tok0);
-    const int nft = (ntok + 15) >> 4;
+    const int nft = (ntok + MS - 1) / MS;
 
-    // weight rows of this lane, one per fragment
+    // first weight row of each fragment (uniform); SwiGLU pairs gate
+    // fragment f with up fragment f + RF/2, N/2 rows further
     int frow[RF];
     bool fval[RF];
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
-      if (a.swiglu) {
-        const int hf = f % (RF / 2);
-        const int gate0 = rt * (BN / 2) + (wave * (RF / 2) + hf) * 16;
+      if constexpr (SWIGLU) {
+        const int gate0 = rt * (BN / 2) + (wave * (RF / 2) + f % (RF / 2)) * MS;
         fval[f] = gate0 < half;
-        frow[f] = (f < RF / 2 ? gate0 : half + gate0) + r16;
+        frow[f] = f < RF / 2 ? gate0 : half + gate0;
       } else {
-        const int r0 = rt * BN + (wave * RF + f) * 16;
-        fval[f] = r0 < N;
-        frow[f] = r0 + r16;
+        frow[f] = rt * BN + (wave * RF + f) * MS;
+        fval[f] = frow[f] < N;
       }
     }
+    const size_t erow = (size_t)e * N;
+    const uint8_t *vb = a.values + erow * vrow, *mb = a.masks + erow * mrow,
+                  *sb = a.scales + erow * srow;
+    uint32_t fv[RF], fm[RF], fs[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      const uint32_t r = fval[f] ? (uint32_t)frow[f] : 0u;
+      fv[f] = r * (uint32_t)vrow;
+      fm[f] = r * (uint32_t)mrow;
+      fs[f] = r * (uint32_t)srow;
+    }
 
-    f32x4_t acc[RF][TF];
+    // Token tile of a chunk: each 1 KB direct-to-LDS load of this wave
+    // covers 64/UPR token rows; lane L fetches unit (L % UPR) ^ (row % UPR)
+    // of its row, so that it lands in the swizzled slot mma_chunk reads.
+    // Rows past the tile repeat the last routed row and positions past K
+    // repeat the last 8; their products only reach unstored outputs or meet
+    // zero weights.
+    const uint16_t *xb = a.x + (size_t)tok0 * K;
+    auto load_tok = [&](uint16_t *buf, int k0) {
 #pragma unroll
-    for (int f = 0; f < RF; ++f)
+      for (int j = 0; j < BPW; ++j) {
+        const int row = (wave * BPW + j) * (64 / UPR) + lane / UPR;
+        const int c = (lane % UPR) ^ (row % UPR);
+        const int kk = min(k0 + c * 8, K - 8);
+        const uint32_t off = (uint32_t)min(row, ntok - 1) * (uint32_t)K + (uint32_t)kk;
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void *)(xb + off),
+            (__attribute__((address_space(3))) void *)(buf + (wave * BPW + j) * 512), 16, 0, 0);
+      }
+    };
+    auto wok = [&](int k0, bool (&ok)[RF]) {
 #pragma unroll
-      for (int t = 0; t < TF; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < RF; ++f) ok[f] = fval[f] && (k0 + KQ * q < K);
+      return k0 + KQ * q + KQ <= K;
+    };
 
-    for (int k0 = 0; k0 < K; k0 += KC) {
-      // compressed weights of this lane's K block, one load each
-      const int kb = k0 + 32 * q;
-      uint2 vv[RF];
-      uint32_t mm[RF];
-      float ss[RF];
-#pragma unroll
-      for (int f = 0; f < RF; ++f) {
-        vv[f] = make_uint2(0, 0);
-        mm[f] = 0;
-        ss[f] = 0.f;
-        if (fval[f] && kb < K) {
-          const size_t row = (size_t)e * N + frow[f];
-          vv[f] = *reinterpret_cast<const uint2 *>(a.values + row * vrow + (kb >> 2));
-          mm[f] = *reinterpret_cast<const uint32_t *>(a.masks + row * mrow + (kb >> 3));
-          ss[f] = e4m3_to_f32(a.scales[row * srow + (kb >> 5)]);
-        }
+    // One K loop + epilogue per path: full token tiles run without any
+    // per-fragment test, partial tiles skip the empty fragments.  The
+    // accumulators live inside each path, so they are never merged.
+    auto run_item = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      typename MF::C acc[RF][TF];
+  #pragma unroll
+      for (int f = 0; f < RF; ++f)
+  #pragma unroll
+        for (int t = 0; t < TF; ++t)
+  #pragma unroll
+          for (int i = 0; i < MF::NC; ++i) acc[f][t][i] = 0.f;
+
+      WChunk<RF, KQ> wc;
+      {
+        bool ok[RF];
+        const bool whole = wok(0, ok);
+        load_wchunk(wc, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, 0);
+        load_tok(tok[0], 0);
       }
-      // routed tokens of this chunk -> LDS (zero outside the tile and K)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      for (int u = tid; u < BM * (KC / 8); u += THREADS) {
-        const int row = u / (KC / 8), c8 = u % (KC / 8);
-        const int kk = k0 + c8 * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < ntok && kk < K)
-          v = *reinterpret_cast<const uint4 *>(a.x + (size_t)(tok0 + row) * K + kk);
-        *reinterpret_cast<uint4 *>(&tok[row * PITCH + c8 * 8]) = v;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint4 A[RF];
-#pragma unroll
-        for (int f = 0; f < RF; ++f) {
-          const uint32_t m8 = (mm[f] >> (8 * s)) & 0xffu;
-          const uint32_t vw = (s < 2) ? vv[f].x : vv[f].y;
-          A[f] = (s & 1) ? decode_group<2>(m8, vw, ss[f], lut) : decode_group<0>(m8, vw, ss[f], lut);
+      for (int c = 0; c < nk; ++c) {
+        const bool more = c + 1 < nk;
+        WChunk<RF, KQ> wn;
+        if (more) {
+          bool ok[RF];
+          const bool whole = wok((c + 1) * KC, ok);
+          load_wchunk(wn, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, (c + 1) * KC);
+          load_tok(tok[(c + 1) & 1], (c + 1) * KC);
         }
-#pragma unroll
-        for (int t = 0; t < TF; ++t) {
-          if (t < nft) {
-            const uint4 B = *reinterpret_cast<const uint4 *>(
-                &tok[(t * 16 + r16) * PITCH + 32 * q + 8 * s]);
-#pragma unroll
-            for (int f = 0; f < RF; ++f)
-              acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[f]), as_bf16x8(B),
-                                                                  acc[f][t], 0, 0, 0);
+        mma_chunk<MS, RF, TF, KC, FULL>(acc, tok[c & 1], wc, lut, nft, q, rl);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (more) wc = wn;
+      }
+
+      // Epilogue.  Accumulator element r of a lane holds weight row
+      // (r/4)*4*LG + 4q + r%4 of its fragment for token rl of its token
+      // fragment: four consecutive rows per group of four, one 8-byte store.
+      const float g = a.gscale[e];
+  #pragma unroll
+      for (int t = 0; t < TF; ++t) {
+        const int trow = t * MS + rl;
+        if (trow >= ntok) continue;
+        const size_t out_r = (size_t)(tok0 + trow);
+  #pragma unroll
+        for (int r4 = 0; r4 < MF::NC / 4; ++r4) {
+          const int roff = r4 * 4 * LG + 4 * q;
+          if constexpr (!SWIGLU) {
+  #pragma unroll
+            for (int f = 0; f < RF; ++f) {
+              if (!fval[f]) continue;
+              const typename MF::C &c = acc[f][t];
+              uint2 o;
+              o.x = pack_bf16x2(g * c[4 * r4 + 0], g * c[4 * r4 + 1]);
+              o.y = pack_bf16x2(g * c[4 * r4 + 2], g * c[4 * r4 + 3]);
+              *reinterpret_cast<uint2 *>(a.y + out_r * N + (frow[f] + roff)) = o;
+            }
+          } else {
+  #pragma unroll
+            for (int f = 0; f < RF / 2; ++f) {
+              if (!fval[f]) continue;
+              const typename MF::C &gt = acc[f][t], &up = acc[f + RF / 2][t];
+              float h[4];
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) h[i] = silu_f32(g * gt[4 * r4 + i]) * (g * up[4 * r4 + i]);
+              uint2 o;
+              o.x = pack_bf16x2(h[0], h[1]);
+              o.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2 *>(a.y + out_r * half + (frow[f] + roff)) = o;
+            }
           }
         }
       }
-    }
-
-    // epilogue: lane holds rows 4q..4q+3 of each fragment for token r16
-    const float g = a.gscale[e];
-#pragma unroll
-    for (int t = 0; t < TF; ++t) {
-      const int trow = t * 16 + r16;
-      if (t >= nft || trow >= ntok) continue;
-      const size_t out_r = (size_t)(tok0 + trow);
-      if (!a.swiglu) {
-#pragma unroll
-        for (int f = 0; f < RF; ++f) {
-          if (!fval[f]) continue;
-          const int n0 = frow[f] - r16 + 4 * q;
-          const f32x4_t c = acc[f][t];
-          uint2 o;
-          o.x = pack_bf16x2(g * c[0], g * c[1]);
-          o.y = pack_bf16x2(g * c[2], g * c[3]);
-          *reinterpret_cast<uint2 *>(a.y + out_r * N + n0) = o;
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < RF / 2; ++f) {
-          if (!fval[f]) continue;
-          const int c0 = frow[f] - r16 + 4 * q;
-          const f32x4_t gt = acc[f][t], up = acc[f + RF / 2][t];
-          float h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = silu_f32(g * gt[i]) * (g * up[i]);
-          uint2 o;
-          o.x = pack_bf16x2(h[0], h[1]);
-          o.y = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<uint2 *>(a.y + out_r * half + c0) = o;
-        }
-      }
-    }
+    };
+    if (nft == TF)
+      run_item(std::true_type{});
+    else
+      run_item(std::false_type{});
   }
 }
 
-template <int WAVES, int RF, int TF>
-static moesq_status_t launch_spgemm(const SpgemmArgs &base, hipStream_t stream) {
-  constexpr int BM = TF * 16, BN = WAVES * RF * 16;
-  SpgemmArgs a = base;
-  a.row_tiles = a.swiglu ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU>
+static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
+  constexpr int BM = TF * MS, BN = WAVES * RF * MS;
+  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU>;
+  a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   // upper bound of the item count: every expert may hold one partial tile
-  const long long tiles = (long long)a.M / BM + std::min(a.E, a.M);
-  long long grid = tiles * a.row_tiles;
-  const long long cap = (long long)device_cu_count() * 4;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((spgemm_kernel<WAVES, RF, TF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, a);
+  const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
+  static thread_local int occ_dev = -1, occ = 1;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (occ_dev != dev) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, WAVES * 64, 0) != hipSuccess ||
+        o < 1)
+      o = 1;
+    occ = o;
+    occ_dev = dev;
+  }
+  long long grid = (long long)device_cu_count() * occ;
+  if (grid > items) grid = items;
+  grid = (grid + 7) & ~7ll;          // XCD-major item spreading needs a multiple of 8
+  if (grid < 8) grid = 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
   return launch_status("moesq_grouped_spgemm");
+}
+
+// Tile choice.  Few routed rows per expert (decode): 16-token fragments,
+// 32-token tiles, 256-position chunks (wide weight loads), two waves per
+// SIMD -- the kernel streams weights.  Otherwise 32x32x16 MFMAs on 128
+// weight rows x 128 tokens per wave, one wave per SIMD with the 256
+// accumulators in AGPRs, so that every decoded weight feeds 4 MFMAs of
+// 32 tokens.  Fragments are whole: the 32-row variant needs the output
+// rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the 16-row
+// variant runs.
+static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
+  const int out_rows = swiglu ? a.N / 2 : a.N;
+  const bool small = (long long)a.M < 16ll * a.E || out_rows % 32 != 0;
+  if (small)
+    return swiglu ? launch_one<8, 16, 4, 2, 256, true>(a, stream)
+                  : launch_one<8, 16, 4, 2, 256, false>(a, stream);
+  return swiglu ? launch_one<4, 32, 4, 4, 128, true>(a, stream)
+                : launch_one<4, 32, 4, 4, 128, false>(a, stream);
 }
 
 static moesq_status_t check_weights(const moesq_weights_t *w, const char *who) {
@@ -252,8 +457,10 @@ static moesq_status_t check_weights(const moesq_weights_t *w, const char *who) {
   if (w->E < 1 || w->E > MOESQ_MAX_EXPERTS)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": E must be in [1, " +
                                      std::to_string(MOESQ_MAX_EXPERTS) + "]");
-  if (w->N < 16 || w->N % 16) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": N must be a positive multiple of 16");
-  if (w->K < 32 || w->K % 32) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": K must be a positive multiple of 32");
+  if (w->N < 16 || w->N % 16)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": N must be a positive multiple of 16");
+  if (w->K < 32 || w->K % 32)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": K must be a positive multiple of 32");
   return MOESQ_OK;
 }
 
@@ -293,6 +500,5 @@ extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
   a.E = w->E;
   a.N = w->N;
   a.K = w->K;
-  a.swiglu = epilogue == MOESQ_EPI_SWIGLU;
-  return launch_spgemm<4, 4, 4>(a, stream);
+  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, stream);
 }

@@ -50,10 +50,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain gather copy of known size (moesq_unpermute without "
+                         "weights over 512 MiB in, 512 MiB out) to scale HBM byte counters")
     return ap.parse_args()
 
 
+def calibrate_copy(m, reps=3):
+    """A copy kernel of known traffic: every row of a [65536, 4096] bf16
+    tensor is read once and written once (512 MiB each way)."""
+    rows, n = 65536, 4096
+    dev = torch.device("cuda")
+    y = torch.ones(rows, n, dtype=torch.bfloat16, device=dev)
+    inv = torch.randperm(rows, device=dev).to(torch.int32)
+    out = torch.empty_like(y)
+    for _ in range(reps):
+        m.moesq_unpermute(y, inv, None, rows, 1, n, out)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "gather copy", "bytes_read_per_launch": rows * n * 2,
+                      "bytes_written_per_launch": rows * n * 2, "launches": reps}))
+
+
 def pack_on_gpu(m, wl, proj, chunk=16):
+    """Dense weights drawn on the GPU, packed (canonical) and re-laid in the
+    tiled layout the GEMM streams best."""
     _, N, K = wl.proj[proj]
     w = m.Weights.empty(wl.E, N, K)
     for c0 in range(0, wl.E, chunk):
@@ -62,8 +82,10 @@ def pack_on_gpu(m, wl, proj, chunk=16):
         m.moesq_pack_weights(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1],
                              w.scales[c0:c1], w.global_scale[c0:c1])
         del dense
+    t = m.tile_weights(w)
     torch.cuda.synchronize()
-    return w
+    del w
+    return t
 
 
 class Step:
@@ -185,6 +207,9 @@ def main():
               "(one process drives one GPU; expert sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
     from sparse_fp4_expert_amd import moesq as m
+    if args.calibrate_copy:
+        calibrate_copy(m)
+        return
     wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     step = Step(m, wl)

@@ -64,6 +64,7 @@ typedef enum {
 } moesq_epilogue_t;
 
 #define MOESQ_LAYOUT_CANONICAL 0
+#define MOESQ_LAYOUT_TILED 1
 
 /* Limits of this build. */
 #define MOESQ_MAX_EXPERTS 1024
@@ -96,8 +97,22 @@ typedef struct {
   const uint8_t *scales;
   const float *global_scale;
   int32_t E, N, K;
-  int32_t layout; /* MOESQ_LAYOUT_CANONICAL */
+  int32_t layout; /* MOESQ_LAYOUT_CANONICAL or MOESQ_LAYOUT_TILED */
 } moesq_weights_t;
+
+/*
+ * MOESQ_LAYOUT_TILED: the same bytes as the canonical layout, permuted so
+ * that the GEMM's loads are whole cache lines.  Needs N % 32 == 0 and
+ * K % 64 == 0.  For expert e, row n = 32*b + r (0 <= r < 32) and segment
+ * j = k/64 (64 logical weights = 8 groups = 2 scale blocks):
+ *
+ *   values [E][N/32][K/64][32][16]  the 16 value bytes of row n for k in [64j, 64j+64)
+ *   masks  [E][N/32][K/64][32][8]   its 8 mask bytes
+ *   scales [E][N/32][K/64][32][2]   its 2 scale bytes
+ *
+ * Inside a segment the byte order is the canonical one.  Sizes per array
+ * equal the canonical sizes.
+ */
 
 /*
  * Routing plan (stable counting sort of the flat top-k ids).
@@ -180,7 +195,17 @@ moesq_status_t moesq_pack_weights(const float *dense, int32_t E, int32_t N, int3
                                   float *global_scale, hipStream_t stream);
 
 /*
- * Decode one expert to dense bf16 WITHOUT the global scale:
+ * Re-lay canonical weights into MOESQ_LAYOUT_TILED (a pure byte permutation).
+ *   src: canonical descriptor (host struct, device buffers).  values, masks,
+ *   scales: device outputs of the canonical sizes; they must not alias src.
+ *   The global scales are not touched (share src->global_scale).
+ * Limits: N % 32 == 0, K % 64 == 0.
+ */
+moesq_status_t moesq_tile_weights(const moesq_weights_t *src, uint8_t *values, uint8_t *masks,
+                                  uint8_t *scales, hipStream_t stream);
+
+/*
+ * Decode one expert to dense bf16 WITHOUT the global scale (either layout):
  *   dense[n][k] = E2M1(code) * E4M3(scale) (exact in bf16) or 0.
  * Uses the same in-register decoder as moesq_grouped_spgemm; meant for
  * checking and debugging.  dense is [N][K] bf16.  0 <= expert < E.

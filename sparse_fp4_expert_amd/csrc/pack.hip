@@ -135,19 +135,56 @@ __global__ __launch_bounds__(PACK_THREADS) void quantize_kernel(
   }
 }
 
+// Canonical -> tiled: one thread per (expert, 32-row block, 64-position
+// segment, row), in tiled order, moving the row's 16 value, 8 mask and 2
+// scale bytes of that segment.
+__global__ __launch_bounds__(PACK_THREADS) void tile_kernel(
+    const uint8_t *__restrict__ sv, const uint8_t *__restrict__ sm, const uint8_t *__restrict__ ss,
+    int E, int N, int K, uint8_t *__restrict__ dv, uint8_t *__restrict__ dm,
+    uint8_t *__restrict__ ds) {
+  const long long t = (long long)blockIdx.x * PACK_THREADS + threadIdx.x;
+  const int J = K / 64, NB = N / 32;
+  const long long total = (long long)E * NB * J * 32;
+  if (t >= total) return;
+  const int r = (int)(t & 31);
+  const long long u = t >> 5;                 // (e*NB + b)*J + j
+  const int j = (int)(u % J);
+  const long long eb = u / J;                 // e*NB + b
+  const long long row = (eb / NB) * N + (eb % NB) * 32 + r;   // e*N + n
+  const uint4 v = *reinterpret_cast<const uint4 *>(sv + row * (K / 4) + j * 16);
+  const uint2 m = *reinterpret_cast<const uint2 *>(sm + row * (K / 8) + j * 8);
+  const uint16_t s = *reinterpret_cast<const uint16_t *>(ss + row * (K / 32) + j * 2);
+  *reinterpret_cast<uint4 *>(dv + t * 16) = v;
+  *reinterpret_cast<uint2 *>(dm + t * 8) = m;
+  *reinterpret_cast<uint16_t *>(ds + t * 2) = s;
+}
+
 // dense[n][8g .. 8g+8) = decoded group g of row n of one expert (bf16, no
-// global scale).
+// global scale), from either layout.
 __global__ __launch_bounds__(PACK_THREADS) void decode_kernel(
-    const uint16_t *__restrict__ values, const uint8_t *__restrict__ masks,
-    const uint8_t *__restrict__ scales, long long groups, uint4 *__restrict__ dense) {
+    const uint8_t *__restrict__ values, const uint8_t *__restrict__ masks,
+    const uint8_t *__restrict__ scales, int N, int K, int tiled, uint4 *__restrict__ dense) {
   __shared__ uint4 lut[256];
   build_group_lut(lut);
   __syncthreads();
   const long long G = (long long)blockIdx.x * PACK_THREADS + threadIdx.x;
+  const long long groups = (long long)N * K / 8;
   if (G >= groups) return;
-  const uint32_t v = values[G];
-  const float s = e4m3_to_f32(scales[G >> 2]);
-  dense[G] = decode_group<0>(masks[G], v, s, lut);
+  long long vo, mo, so;
+  if (tiled) {
+    const int n = (int)(G / (K / 8)), g = (int)(G % (K / 8));
+    const long long seg = ((long long)(n / 32) * (K / 64) + g / 8) * 32 + (n % 32);
+    vo = seg * 16 + (g % 8) * 2;
+    mo = seg * 8 + (g % 8);
+    so = seg * 2 + (g % 8) / 4;
+  } else {
+    vo = G * 2;
+    mo = G;
+    so = G >> 2;
+  }
+  const uint32_t v = *reinterpret_cast<const uint16_t *>(values + vo);
+  const float s = e4m3_to_f32(scales[so]);
+  dense[G] = decode_group<0>(masks[mo], v, s, lut);
 }
 
 }  // namespace moesq
@@ -180,22 +217,45 @@ extern "C" moesq_status_t moesq_pack_weights(const float *dense, int32_t E, int3
   return launch_status("moesq_pack_weights");
 }
 
+extern "C" moesq_status_t moesq_tile_weights(const moesq_weights_t *src, uint8_t *values,
+                                             uint8_t *masks, uint8_t *scales, hipStream_t stream) {
+  clear_error();
+  if (!src || !values || !masks || !scales)
+    return fail(MOESQ_ERR_NULL, "moesq_tile_weights: NULL pointer");
+  if (src->layout != MOESQ_LAYOUT_CANONICAL)
+    return fail(MOESQ_ERR_LAYOUT, "moesq_tile_weights: source must be canonical");
+  if (!src->values || !src->masks || !src->scales)
+    return fail(MOESQ_ERR_NULL, "moesq_tile_weights: NULL weight buffer");
+  if (src->E < 1 || src->N < 32 || src->N % 32 || src->K < 64 || src->K % 64)
+    return fail(MOESQ_ERR_SHAPE, "moesq_tile_weights: need E >= 1, N % 32 == 0, K % 64 == 0");
+  const long long total = (long long)src->E * (src->N / 32) * (src->K / 64) * 32;
+  const long long blocks = (total + PACK_THREADS - 1) / PACK_THREADS;
+  if (blocks >= (1ll << 31)) return fail(MOESQ_ERR_SHAPE, "moesq_tile_weights: too large");
+  hipLaunchKernelGGL(tile_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, stream,
+                     src->values, src->masks, src->scales, src->E, src->N, src->K, values, masks,
+                     scales);
+  return launch_status("moesq_tile_weights");
+}
+
 extern "C" moesq_status_t moesq_decode_weights(const moesq_weights_t *w, int32_t expert,
                                                uint16_t *dense, hipStream_t stream) {
   clear_error();
   if (!w || !dense) return fail(MOESQ_ERR_NULL, "moesq_decode_weights: NULL pointer");
-  if (w->layout != MOESQ_LAYOUT_CANONICAL)
+  if (w->layout != MOESQ_LAYOUT_CANONICAL && w->layout != MOESQ_LAYOUT_TILED)
     return fail(MOESQ_ERR_LAYOUT, "moesq_decode_weights: unknown layout");
   if (!w->values || !w->masks || !w->scales)
     return fail(MOESQ_ERR_NULL, "moesq_decode_weights: NULL weight buffer");
   if (w->E < 1 || w->N < 1 || w->K < 32 || w->K % 32)
     return fail(MOESQ_ERR_SHAPE, "moesq_decode_weights: bad E/N/K");
+  if (w->layout == MOESQ_LAYOUT_TILED && (w->N % 32 || w->K % 64))
+    return fail(MOESQ_ERR_SHAPE, "moesq_decode_weights: tiled layout needs N % 32 == 0, K % 64 == 0");
   if (expert < 0 || expert >= w->E)
     return fail(MOESQ_ERR_ARG, "moesq_decode_weights: expert out of range");
   const long long groups = (long long)w->N * w->K / 8;
   const long long g0 = (long long)expert * groups;
   hipLaunchKernelGGL(decode_kernel, dim3((unsigned)((groups + PACK_THREADS - 1) / PACK_THREADS)),
-                     dim3(PACK_THREADS), 0, stream, (const uint16_t *)w->values + g0,
-                     w->masks + g0, w->scales + g0 / 4, groups, (uint4 *)dense);
+                     dim3(PACK_THREADS), 0, stream, w->values + g0 * 2, w->masks + g0,
+                     w->scales + g0 / 4, w->N, w->K, (int)(w->layout == MOESQ_LAYOUT_TILED),
+                     (uint4 *)dense);
   return launch_status("moesq_decode_weights");
 }

@@ -78,21 +78,23 @@ struct WChunk {
 
 // vb/mb/sb: the expert's value/mask/scale bases; fv/fm/fs: byte offsets of
 // each fragment's first row (uniform); vo/mo/so: this lane's offsets inside
-// a fragment (its row and lane group).  ok[f]: the lane's first scale block
-// lies inside K; two-block ranges load only the first block when `whole` is
-// false (K ends in the middle of the range).
+// a fragment (its row and lane group); kv/km/ks: offsets of the chunk.
+// ok[f]: the lane's first scale block lies inside K; two-block ranges load
+// only the first block when `whole` is false (K ends in the middle of the
+// range).
 template <int RF, int KQ>
 __device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb,
                                             const uint8_t *mb, const uint8_t *sb,
                                             const uint32_t (&fv)[RF], const uint32_t (&fm)[RF],
                                             const uint32_t (&fs)[RF], uint32_t vo, uint32_t mo,
-                                            uint32_t so, const bool (&ok)[RF], bool whole, int k0) {
+                                            uint32_t so, const bool (&ok)[RF], bool whole,
+                                            uint32_t kv, uint32_t km, uint32_t ks) {
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
     if (KQ == 64 && ok[f] && !whole) {
-      const uint8_t *pv = vb + (fv[f] + vo + (k0 >> 2));
-      const uint8_t *pm = mb + (fm[f] + mo + (k0 >> 3));
-      const uint8_t *ps = sb + (fs[f] + so + (k0 >> 5));
+      const uint8_t *pv = vb + (fv[f] + vo + kv);
+      const uint8_t *pm = mb + (fm[f] + mo + km);
+      const uint8_t *ps = sb + (fs[f] + so + ks);
       const uint2 v = *reinterpret_cast<const uint2 *>(pv);
       w.v[f][0] = v.x;
       w.v[f][1] = v.y;
@@ -103,9 +105,9 @@ __device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb
       for (int i = 1; i < WChunk<RF, KQ>::MD; ++i) w.m[f][i] = 0;
       w.s[f] = *ps;
     } else if (ok[f]) {
-      const uint8_t *pv = vb + (fv[f] + vo + (k0 >> 2));
-      const uint8_t *pm = mb + (fm[f] + mo + (k0 >> 3));
-      const uint8_t *ps = sb + (fs[f] + so + (k0 >> 5));
+      const uint8_t *pv = vb + (fv[f] + vo + kv);
+      const uint8_t *pm = mb + (fm[f] + mo + km);
+      const uint8_t *ps = sb + (fs[f] + so + ks);
       if constexpr (KQ == 32) {
         const uint2 v = *reinterpret_cast<const uint2 *>(pv);
         w.v[f][0] = v.x;
@@ -186,7 +188,7 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, bool TILED>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void spgemm_kernel(
     SpgemmArgs a) {
@@ -202,6 +204,7 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
   static_assert(64 % UPR == 0, "a 1 KB load covers whole token rows");
   static_assert(RF % 2 == 0, "SwiGLU pairs gate and up fragments");
   static_assert(KQ == 32 || KQ == 64, "a lane group covers one or two scale blocks");
+  static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
 
   __shared__ uint4 lut[256];
   __shared__ int s_lo[MOESQ_MAX_EXPERTS + 1];
@@ -243,9 +246,12 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
   const int half = N >> 1;
   const size_t vrow = (size_t)(K >> 2), mrow = (size_t)(K >> 3), srow = (size_t)(K >> 5);
   const int nk = (K + KC - 1) / KC;
-  const uint32_t vo = (uint32_t)rl * (uint32_t)vrow + (KQ / 4) * q;
-  const uint32_t mo = (uint32_t)rl * (uint32_t)mrow + (KQ / 8) * q;
-  const uint32_t so = (uint32_t)rl * (uint32_t)srow + (KQ / 32) * q;
+  // this lane's offsets inside a fragment: canonical rows are K/4, K/8, K/32
+  // bytes long; tiled segments hold 32 rows of 16, 8, 2 bytes
+  const uint32_t vo = TILED ? q * 512u + rl * 16u : (uint32_t)rl * (uint32_t)vrow + (KQ / 4) * q;
+  const uint32_t mo = TILED ? q * 256u + rl * 8u : (uint32_t)rl * (uint32_t)mrow + (KQ / 8) * q;
+  const uint32_t so = TILED ? q * 64u + rl * 2u : (uint32_t)rl * (uint32_t)srow + (KQ / 32) * q;
+  const uint32_t segs = (uint32_t)(K >> 6);
 
   // Items of one round of workgroups are spread XCD-major: the grid is a
   // multiple of 8 and workgroup b runs on XCD b % 8, so consecutive items
@@ -291,10 +297,30 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
       const uint32_t r = fval[f] ? (uint32_t)frow[f] : 0u;
-      fv[f] = r * (uint32_t)vrow;
-      fm[f] = r * (uint32_t)mrow;
-      fs[f] = r * (uint32_t)srow;
+      if constexpr (TILED) {
+        const uint32_t blk = (r >> 5) * segs, rin = r & 31u;
+        fv[f] = blk * 512u + rin * 16u;
+        fm[f] = blk * 256u + rin * 8u;
+        fs[f] = blk * 64u + rin * 2u;
+      } else {
+        fv[f] = r * (uint32_t)vrow;
+        fm[f] = r * (uint32_t)mrow;
+        fs[f] = r * (uint32_t)srow;
+      }
     }
+    // chunk offsets: canonical advances k/4, k/8, k/32 bytes; tiled advances
+    // one 64-position segment (512, 256, 64 bytes) per 64 positions
+    auto koff = [&](int k0, uint32_t &kv, uint32_t &km, uint32_t &ks) {
+      if constexpr (TILED) {
+        kv = (uint32_t)k0 * 8u;
+        km = (uint32_t)k0 * 4u;
+        ks = (uint32_t)k0;
+      } else {
+        kv = (uint32_t)k0 >> 2;
+        km = (uint32_t)k0 >> 3;
+        ks = (uint32_t)k0 >> 5;
+      }
+    };
 
     // Token tile of a chunk: each 1 KB direct-to-LDS load of this wave
     // covers 64/UPR token rows; lane L fetches unit (L % UPR) ^ (row % UPR)
@@ -338,7 +364,9 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
       {
         bool ok[RF];
         const bool whole = wok(0, ok);
-        load_wchunk(wc, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, 0);
+        uint32_t kv, km, ks;
+        koff(0, kv, km, ks);
+        load_wchunk(wc, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
         load_tok(tok[0], 0);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -349,7 +377,9 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
         if (more) {
           bool ok[RF];
           const bool whole = wok((c + 1) * KC, ok);
-          load_wchunk(wn, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, (c + 1) * KC);
+          uint32_t kv, km, ks;
+          koff((c + 1) * KC, kv, km, ks);
+          load_wchunk(wn, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
           load_tok(tok[(c + 1) & 1], (c + 1) * KC);
         }
         mma_chunk<MS, RF, TF, KC, FULL>(acc, tok[c & 1], wc, lut, nft, q, rl);
@@ -404,10 +434,10 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, bool TILED>
 static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
-  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU>;
+  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, TILED>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   // upper bound of the item count: every expert may hold one partial tile
   const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
@@ -438,20 +468,28 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // 32 tokens.  Fragments are whole: the 32-row variant needs the output
 // rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the 16-row
 // variant runs.
-static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
+template <bool TILED>
+static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
   const bool small = (long long)a.M < 16ll * a.E || out_rows % 32 != 0;
   if (small)
-    return swiglu ? launch_one<8, 16, 4, 2, 256, true>(a, stream)
-                  : launch_one<8, 16, 4, 2, 256, false>(a, stream);
-  return swiglu ? launch_one<4, 32, 4, 4, 128, true>(a, stream)
-                : launch_one<4, 32, 4, 4, 128, false>(a, stream);
+    return swiglu ? launch_one<8, 16, 4, 2, 256, true, TILED>(a, stream)
+                  : launch_one<8, 16, 4, 2, 256, false, TILED>(a, stream);
+  return swiglu ? launch_one<4, 32, 4, 4, 128, true, TILED>(a, stream)
+                : launch_one<4, 32, 4, 4, 128, false, TILED>(a, stream);
+}
+
+static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, bool tiled,
+                                    hipStream_t stream) {
+  return tiled ? launch_layout<true>(a, swiglu, stream) : launch_layout<false>(a, swiglu, stream);
 }
 
 static moesq_status_t check_weights(const moesq_weights_t *w, const char *who) {
   if (!w) return fail(MOESQ_ERR_NULL, std::string(who) + ": weight descriptor is NULL");
-  if (w->layout != MOESQ_LAYOUT_CANONICAL)
+  if (w->layout != MOESQ_LAYOUT_CANONICAL && w->layout != MOESQ_LAYOUT_TILED)
     return fail(MOESQ_ERR_LAYOUT, std::string(who) + ": unknown weight layout");
+  if (w->layout == MOESQ_LAYOUT_TILED && (w->N % 32 || w->K % 64))
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": tiled layout needs N % 32 == 0, K % 64 == 0");
   if (!w->values || !w->masks || !w->scales || !w->global_scale)
     return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL weight buffer");
   if (w->E < 1 || w->E > MOESQ_MAX_EXPERTS)
@@ -500,5 +538,5 @@ extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
   a.E = w->E;
   a.N = w->N;
   a.K = w->K;
-  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, stream);
+  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout == MOESQ_LAYOUT_TILED, stream);
 }

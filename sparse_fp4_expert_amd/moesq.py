@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_LAYOUT, ERR_HIP, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
 EPI_NONE, EPI_SWIGLU = 0, 1
-LAYOUT_CANONICAL = 0
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 MAX_EXPERTS = 1024
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -52,13 +52,15 @@ _spgemm_ws = _sig("moesq_spgemm_workspace_bytes", _sz, _i32, ctypes.POINTER(Weig
 _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
+_tile = _sig("moesq_tile_weights", _i32, ctypes.POINTER(WeightsDesc), _vp, _vp, _vp, _vp)
 _status_string = _sig("moesq_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moesq_last_error", ctypes.c_char_p)
 _version = _sig("moesq_version", _i32)
 
 EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes", "moesq_unpermute",
-            "moesq_pack_weights", "moesq_decode_weights", "moesq_status_string",
+            "moesq_pack_weights", "moesq_tile_weights", "moesq_decode_weights",
+            "moesq_status_string",
             "moesq_last_error", "moesq_version"]
 
 
@@ -102,12 +104,13 @@ def _stream(stream):
 
 
 class Weights:
-    """Device tensors of compressed experts in the canonical layout.
+    """Device tensors of compressed experts.
 
     values uint8 [E, N, K/4], masks uint8 [E, N, K/8], scales uint8 [E, N, K/32],
-    global_scale float32 [E]."""
+    global_scale float32 [E].  `layout` is LAYOUT_CANONICAL or LAYOUT_TILED (the
+    same shapes; tiled bytes are permuted as include/moesq.h describes)."""
 
-    def __init__(self, values, masks, scales, global_scale):
+    def __init__(self, values, masks, scales, global_scale, layout=LAYOUT_CANONICAL):
         E, N, K4 = values.shape
         self.E, self.N, self.K = int(E), int(N), int(K4) * 4
         for t, shape, name in [(masks, (E, N, self.K // 8), "masks"),
@@ -116,10 +119,11 @@ class Weights:
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
         self.values, self.masks, self.scales, self.global_scale = values, masks, scales, global_scale
+        self.layout = layout
         self.desc = WeightsDesc(_ptr(values, torch.uint8, "values"), _ptr(masks, torch.uint8, "masks"),
                                 _ptr(scales, torch.uint8, "scales"),
                                 _ptr(global_scale, torch.float32, "global_scale"),
-                                self.E, self.N, self.K, LAYOUT_CANONICAL)
+                                self.E, self.N, self.K, layout)
 
     @property
     def nbytes(self) -> int:
@@ -129,11 +133,11 @@ class Weights:
         return self.N * self.K * 13 // 32 + 4
 
     @staticmethod
-    def empty(E: int, N: int, K: int, device="cuda"):
+    def empty(E: int, N: int, K: int, device="cuda", layout=LAYOUT_CANONICAL):
         u8 = dict(dtype=torch.uint8, device=device)
         return Weights(torch.empty(E, N, K // 4, **u8), torch.empty(E, N, K // 8, **u8),
                        torch.empty(E, N, K // 32, **u8),
-                       torch.empty(E, dtype=torch.float32, device=device))
+                       torch.empty(E, dtype=torch.float32, device=device), layout)
 
 
 # ------------------------------------------------------------ C-ABI mirrors
@@ -180,6 +184,12 @@ def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, glo
     _check(_pack(_ptr(dense, torch.float32, "dense"), E, N, K, _ptr(values, torch.uint8, "values"),
                  _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
                  _ptr(global_scale, torch.float32, "global_scale"), _stream(stream)))
+
+
+def moesq_tile_weights(src: Weights, values, masks, scales, stream=None):
+    _check(_tile(ctypes.byref(src.desc), _ptr(values, torch.uint8, "values"),
+                 _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
+                 _stream(stream)))
 
 
 def moesq_decode_weights(w: Weights, expert: int, dense, stream=None):
@@ -231,6 +241,14 @@ def pack_weights(dense, stream=None) -> Weights:
     w = Weights.empty(E, N, K, device=dense.device)
     moesq_pack_weights(dense, E, N, K, w.values, w.masks, w.scales, w.global_scale, stream)
     return w
+
+
+def tile_weights(w: Weights, stream=None) -> Weights:
+    """Canonical Weights -> a new tiled Weights (shares global_scale)."""
+    t = Weights(torch.empty_like(w.values), torch.empty_like(w.masks), torch.empty_like(w.scales),
+                w.global_scale, LAYOUT_TILED)
+    moesq_tile_weights(w, t.values, t.masks, t.scales, stream)
+    return t
 
 
 def decode_weights(w: Weights, expert: int, stream=None):

@@ -98,6 +98,39 @@ def test_pack_extreme_ranges(lib):
         assert np.array_equal(f64(lib.decode_weights(w, e)), oracle.decode(p, include_global=False))
 
 
+def _tiled_ref(arr, nbytes_per_seg):
+    """The tiled permutation written from its definition: [E][N][K/X] ->
+    [E][N/32][K/64][32][bytes per 64-position segment]."""
+    E, N, W = arr.shape
+    J = W // nbytes_per_seg
+    return arr.reshape(E, N // 32, 32, J, nbytes_per_seg).transpose(0, 1, 3, 2, 4).reshape(E, N, W)
+
+
+def test_tile_layout_and_decode(lib):
+    g = torch.Generator().manual_seed(5)
+    E, N, K = 3, 96, 448
+    d = torch.randn(E, N, K, generator=g) * 0.02
+    w = lib.pack_weights(d.cuda())
+    t = lib.tile_weights(w)
+    torch.cuda.synchronize()
+    for name, seg in [("values", 16), ("masks", 8), ("scales", 2)]:
+        a = getattr(w, name).cpu().numpy()
+        b = getattr(t, name).cpu().numpy()
+        assert np.array_equal(b, _tiled_ref(a, seg)), name
+    for e in range(E):
+        p = oracle.quantize(d[e].numpy())
+        assert np.array_equal(f64(lib.decode_weights(t, e)), oracle.decode(p, include_global=False))
+
+
+def test_tile_rejects_shapes(lib):
+    w = lib.pack_weights(torch.zeros(1, 48, 64, device="cuda"))
+    with pytest.raises(lib.MoesqError):
+        lib.tile_weights(w)                       # N % 32 != 0
+    w = lib.pack_weights(torch.zeros(1, 64, 96, device="cuda"))
+    with pytest.raises(lib.MoesqError):
+        lib.tile_weights(w)                       # K % 64 != 0
+
+
 # ------------------------------------------------------------------ routing
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
@@ -184,7 +217,8 @@ def _full_oracle_gemm(ids, E, k, x, packs, swiglu=False, packs2=None, weights=No
     return off, perm, inv, y
 
 
-def test_spgemm_tiny_end_to_end(lib):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_spgemm_tiny_end_to_end(lib, tiled):
     """tiny: route -> permute -> GEMM -> flat and weighted combine, every
     output against the oracle."""
     wl = synth.WORKLOADS["tiny"]
@@ -193,6 +227,8 @@ def test_spgemm_tiny_end_to_end(lib):
     dense = synth.dense_experts(wl, 0)
     packs = [oracle.quantize(dense[e].numpy()) for e in range(wl.E)]
     w = lib.pack_weights(dense.cuda())
+    if tiled:
+        w = lib.tile_weights(w)
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
     xr = lib.permute(x.cuda(), perm, wl.k)
     y = lib.grouped_spgemm(xr, off, w)
@@ -205,7 +241,7 @@ def test_spgemm_tiny_end_to_end(lib):
     tol_check(f64(out), oracle.unpermute(y_ref, inv_r, tw, wl.T, wl.k), "weighted combine")
 
 
-def _edge_case(lib, loads, N, K, swiglu, seed):
+def _edge_case(lib, loads, N, K, swiglu, seed, tiled=False):
     E = len(loads)
     ids = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(loads)])
     rng = np.random.default_rng(seed)
@@ -217,6 +253,8 @@ def _edge_case(lib, loads, N, K, swiglu, seed):
     dense = synth.dense_experts(wl, 0)
     packs = [oracle.quantize(dense[e].numpy()) for e in range(E)]
     w = lib.pack_weights(dense.cuda())
+    if tiled:
+        w = lib.tile_weights(w)
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), E, 1)
     xr = lib.permute(x.cuda(), perm, 1)
     y = lib.grouped_spgemm(xr, off, w, lib.EPI_SWIGLU if swiglu else lib.EPI_NONE)
@@ -224,7 +262,7 @@ def _edge_case(lib, loads, N, K, swiglu, seed):
     _, _, _, y_ref = _full_oracle_gemm(ids, E, 1, x, packs)
     if swiglu:
         y_ref = oracle.bf16_round(oracle.swiglu(y_ref))
-    tol_check(f64(y), y_ref, f"loads={loads} N={N} K={K} swiglu={swiglu}")
+    tol_check(f64(y), y_ref, f"loads={loads} N={N} K={K} swiglu={swiglu} tiled={tiled}")
 
 
 @pytest.mark.parametrize("loads,N,K,swiglu", [
@@ -240,6 +278,18 @@ def test_spgemm_edges(lib, loads, N, K, swiglu):
     _edge_case(lib, loads, N, K, swiglu, seed=sum(loads) + N + K)
 
 
+@pytest.mark.parametrize("loads,N,K,swiglu", [
+    ([0, 1, 15, 16, 17, 33, 130, 0], 64, 128, False),
+    ([0, 1, 15, 16, 17, 33, 130, 0], 128, 192, True),
+    ([0, 0, 0, 200, 0], 288, 320, False),
+    ([5, 0, 64, 127, 128, 129, 1], 32, 448, False),
+    ([1] * 20, 128, 256, True),
+    ([40] * 4, 64, 64, False),
+])
+def test_spgemm_edges_tiled(lib, loads, N, K, swiglu):
+    _edge_case(lib, loads, N, K, swiglu, seed=sum(loads) + N + K + 1, tiled=True)
+
+
 @pytest.mark.parametrize("name", ["decode-30b", "prefill-30b"])
 def test_spgemm_30b_workloads(lib, name):
     """Full-size 30B-class workloads; sampled experts are checked against the
@@ -250,10 +300,11 @@ def test_spgemm_30b_workloads(lib, name):
     x = synth.tokens(wl)
     say(f"[{name}] packing {wl.E} experts on the GPU")
     w = pack_workload(lib, wl, 0)
+    wt = lib.tile_weights(w)
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
     xr = lib.permute(x.cuda(), perm, wl.k)
-    say(f"[{name}] grouped GEMM M={wl.M} N={N} K={K}")
-    y = lib.grouped_spgemm(xr, off, w)
+    say(f"[{name}] grouped GEMM M={wl.M} N={N} K={K} (tiled weights)")
+    y = lib.grouped_spgemm(xr, off, wt)
     torch.cuda.synchronize()
     off_r, perm_r, _ = oracle.route(ids, wl.E)
     counts = np.diff(off_r)
@@ -283,11 +334,12 @@ def test_chain_1t_workloads(lib, name):
     say(f"[{name}] packing 2 x {wl.E} experts on the GPU")
     w1 = pack_workload(lib, wl, 0)
     w2 = pack_workload(lib, wl, 1)
+    w1t, w2t = lib.tile_weights(w1), lib.tile_weights(w2)
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
     xr = lib.permute(x.cuda(), perm, wl.k)
-    say(f"[{name}] chain M={wl.M}")
-    h = lib.grouped_spgemm(xr, off, w1, lib.EPI_SWIGLU)
-    y2 = lib.grouped_spgemm(h, off, w2)
+    say(f"[{name}] chain M={wl.M} (tiled weights)")
+    h = lib.grouped_spgemm(xr, off, w1t, lib.EPI_SWIGLU)
+    y2 = lib.grouped_spgemm(h, off, w2t)
     tw_d = torch.from_numpy(tw).cuda()
     out = lib.unpermute(y2, inv, tw_d if wl.weighted_combine else None, wl.T, wl.k)
     torch.cuda.synchronize()

@@ -475,8 +475,8 @@ static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_
   if (small)
     return swiglu ? launch_one<8, 16, 4, 2, 256, true, TILED>(a, stream)
                   : launch_one<8, 16, 4, 2, 256, false, TILED>(a, stream);
-  return swiglu ? launch_one<4, 32, 4, 4, 128, true, TILED>(a, stream)
-                : launch_one<4, 32, 4, 4, 128, false, TILED>(a, stream);
+  return swiglu ? launch_one<8, 32, 2, 4, 128, true, TILED>(a, stream)
+                : launch_one<8, 32, 2, 4, 128, false, TILED>(a, stream);
 }
 
 static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, bool tiled,

@@ -116,6 +116,8 @@ class Step:
         self.off = torch.empty(E + 1, **i32)
         self.perm = torch.empty(M, **i32)
         self.inv = torch.empty(M, **i32)
+        nws = m.moesq_route_workspace_bytes(T, k, E)
+        self.route_ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
         self.xr = torch.empty(M, wl.K_in, **bf)
         if wl.swiglu:
             self.h = torch.empty(M, wl.proj[0][1] // 2, **bf)
@@ -130,7 +132,8 @@ class Step:
         self.w = self.replicas[self.turn % len(self.replicas)]
         self.turn += 1
         calls = [
-            lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm, self.inv),
+            lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm, self.inv,
+                                  self.route_ws),
             lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr),
         ]
         if wl.swiglu:

@@ -5,17 +5,22 @@
 // paper summary page, "3.4 Implementation details"), so the routed rows are
 // grouped by expert first: a stable counting sort of the flat top-k ids.
 //
-// One workgroup of ROUTE_WAVES wavefronts.  Wave w owns the contiguous slice
-// [w*C, (w+1)*C) of the flat ids and walks it 64 ids at a time.  Inside a
-// batch, lanes holding the same expert find each other with one ballot per
-// id bit (a wave-wide multi-split); the lowest such lane is the leader, and
-// a lane's rank among its peers is the popcount of peers below it.
+// A wave owns a contiguous slice of the flat ids and walks it 64 ids at a
+// time.  Inside a batch, lanes holding the same expert find each other with
+// one ballot per id bit (a wave-wide multi-split); the lowest such lane is
+// the leader, and a lane's rank among its peers is the popcount of peers
+// below it.
 //   pass 1: per-wave expert histograms in LDS (leaders add their peer count)
-//   scan:   per expert, exclusive prefix over waves; then exclusive prefix
-//           over experts -> offsets
-//   pass 2: same walk again; row = offset[e] + base[w][e] + running + rank
+//   scan:   per expert, exclusive prefix over waves (and blocks); then
+//           exclusive prefix over experts -> offsets
+//   pass 2: same walk again; row = base[w][e] + running + rank
 // Every step is in index order, so perm is the stable order and the result
 // is bit-identical on every run (no atomics).
+//
+// Small inputs run all of it in one workgroup.  Large ones split the ids
+// into blocks of ROUTE_BLOCK_IDS: a histogram kernel per block, one scan
+// kernel over (block, expert) counts in the workspace, and a scatter kernel
+// per block.
 #include "common.hpp"
 
 namespace moesq {
@@ -34,26 +39,10 @@ __device__ __forceinline__ uint64_t peers_of(int e, int nbits, uint64_t active) 
   return peers;
 }
 
-__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__restrict__ ids,
-                                                              int M, int E, int32_t *offsets,
-                                                              int32_t *perm, int32_t *inv_perm) {
-  __shared__ int cnt[ROUTE_WAVES][MOESQ_MAX_EXPERTS];
-  __shared__ int off[MOESQ_MAX_EXPERTS + 1];
-  __shared__ int wave_tot[ROUTE_WAVES];
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-
-  for (int i = threadIdx.x; i < ROUTE_WAVES * MOESQ_MAX_EXPERTS; i += ROUTE_THREADS)
-    (&cnt[0][0])[i] = 0;
-  __syncthreads();
-
-  const int chunk = ((M + ROUTE_WAVES - 1) / ROUTE_WAVES + 63) & ~63;
-  const int beg = min(M, w * chunk), end = min(M, beg + chunk);
-
-  // pass 1: histogram of this wave's slice
+// Histogram of ids[beg, end) into cnt[e] by one wave (leaders add).
+__device__ __forceinline__ void wave_count(const int32_t *__restrict__ ids, int beg, int end,
+                                           int E, int nbits, uint64_t lt_mask, int lane,
+                                           int *cnt) {
   for (int base = beg; base < end; base += 64) {
     const int i = base + lane;
     int e = -1;
@@ -63,8 +52,95 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
     }
     const uint64_t active = __ballot(e >= 0);
     const uint64_t peers = peers_of(e, nbits, active);
-    if (e >= 0 && (peers & lt_mask) == 0) cnt[w][e] += __popcll(peers);
+    if (e >= 0 && (peers & lt_mask) == 0) cnt[e] += __popcll(peers);
   }
+}
+
+// Ranks and scatter of ids[beg, end) by one wave; run[e] holds the next
+// routed row of expert e for this wave and advances.
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int beg, int end,
+                                             int E, int nbits, uint64_t lt_mask, int lane,
+                                             int *run, int32_t *perm, int32_t *inv_perm) {
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    int e = -1;
+    if (i < end) {
+      e = ids[i];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t active = __ballot(e >= 0);
+    const uint64_t peers = peers_of(e, nbits, active);
+    int row = -1;
+    if (e >= 0) row = run[e] + __popcll(peers & lt_mask);
+    // all lanes have read run[e]; leaders now advance it
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && (peers & lt_mask) == 0) run[e] += __popcll(peers);
+    if (i < end) {
+      inv_perm[i] = row;
+      if (row >= 0) perm[row] = i;
+    }
+  }
+}
+
+// Exclusive prefix of v[0..n) in place by the whole block; returns the total.
+template <int THREADS>
+__device__ int block_exclusive_scan(int *v, int n, int *wave_tot) {
+  constexpr int WAVES = THREADS / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int per_wave = (n + WAVES - 1) / WAVES;
+  const int e0 = min(n, w * per_wave), e1 = min(n, e0 + per_wave);
+  const int per_lane = (e1 - e0 + 63) / 64;
+  const int l0 = min(e1, e0 + lane * per_lane), l1 = min(e1, l0 + per_lane);
+  int s = 0;
+  for (int e = l0; e < l1; ++e) s += v[e];
+  int incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) wave_tot[w] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+  for (int u = 0; u < WAVES; ++u) {
+    if (u < w) wbase += wave_tot[u];
+    tot += wave_tot[u];
+  }
+  int run = wbase + incl - s;
+  for (int e = l0; e < l1; ++e) {
+    const int c = v[e];
+    v[e] = run;
+    run += c;
+  }
+  __syncthreads();
+  return tot;
+}
+
+__device__ __forceinline__ int id_bits(int E) { return (E > 1) ? 32 - __clz(E - 1) : 0; }
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Whole plan in one workgroup.
+__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__restrict__ ids,
+                                                              int M, int E, int32_t *offsets,
+                                                              int32_t *perm, int32_t *inv_perm) {
+  __shared__ int cnt[ROUTE_WAVES][MOESQ_MAX_EXPERTS];
+  __shared__ int off[MOESQ_MAX_EXPERTS + 1];
+  __shared__ int wave_tot[ROUTE_WAVES];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint64_t lt_mask = lanes_below(lane);
+  const int nbits = id_bits(E);
+
+  for (int i = threadIdx.x; i < ROUTE_WAVES * MOESQ_MAX_EXPERTS; i += ROUTE_THREADS)
+    (&cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  const int chunk = ((M + ROUTE_WAVES - 1) / ROUTE_WAVES + 63) & ~63;
+  const int beg = min(M, w * chunk), end = min(M, beg + chunk);
+  wave_count(ids, beg, end, E, nbits, lt_mask, lane, cnt[w]);
   __syncthreads();
 
   // per expert: exclusive prefix over waves, total in off[e]
@@ -79,76 +155,112 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
     off[e] = run;
   }
   __syncthreads();
-
-  // exclusive prefix over experts: each wave scans a contiguous range of
-  // experts lane-serially, then the wave totals are combined.
-  {
-    const int per_wave = (E + ROUTE_WAVES - 1) / ROUTE_WAVES;
-    const int e0 = min(E, w * per_wave), e1 = min(E, e0 + per_wave);
-    const int per_lane = (e1 - e0 + 63) / 64;
-    const int l0 = min(e1, e0 + lane * per_lane), l1 = min(e1, l0 + per_lane);
-    int s = 0;
-    for (int e = l0; e < l1; ++e) s += off[e];
-    // inclusive wave scan of lane sums
-    int incl = s;
+  const int total = block_exclusive_scan<ROUTE_THREADS>(off, E, wave_tot);
+  if (threadIdx.x == 0) off[E] = total;
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += t;
-    }
-    if (lane == 63) wave_tot[w] = incl;
-    __syncthreads();
-    int wbase = 0;
-    for (int v = 0; v < w; ++v) wbase += wave_tot[v];
-    int run = wbase + incl - s;
-    // rewrite off[] in place as exclusive prefix (each lane owns its range)
-    for (int e = l0; e < l1; ++e) {
-      const int c = off[e];
-      off[e] = run;
-      run += c;
-    }
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int v = 0; v < ROUTE_WAVES; ++v) tot += wave_tot[v];
-      off[E] = tot;
-    }
+    for (int v = 0; v < ROUTE_WAVES; ++v) cnt[v][e] += off[e];
   }
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += ROUTE_THREADS) offsets[e] = off[e];
+  wave_scatter(ids, beg, end, E, nbits, lt_mask, lane, cnt[w], perm, inv_perm);
+}
 
-  // pass 2: ranks and scatter
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    int e = -1;
-    if (i < end) {
-      e = ids[i];
-      if (e < 0 || e >= E) e = -1;
-    }
-    const uint64_t active = __ballot(e >= 0);
-    const uint64_t peers = peers_of(e, nbits, active);
-    int row = -1;
-    if (e >= 0) row = off[e] + cnt[w][e] + __popcll(peers & lt_mask);
-    // all lanes have read cnt[w][e]; leaders now advance it
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0 && (peers & lt_mask) == 0) cnt[w][e] += __popcll(peers);
-    if (i < end) {
-      inv_perm[i] = row;
-      if (row >= 0) perm[row] = i;
-    }
+constexpr int RB_WAVES = 4;
+constexpr int RB_THREADS = RB_WAVES * 64;
+constexpr int ROUTE_BLOCK_IDS = 2048;          // ids per block, 512 per wave
+
+// Large inputs, step 1: counts[b][e] of block b.
+__global__ __launch_bounds__(RB_THREADS) void route_hist_kernel(const int32_t *__restrict__ ids,
+                                                                int M, int E, int *counts) {
+  __shared__ int cnt[RB_WAVES][MOESQ_MAX_EXPERTS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < RB_WAVES * E; i += RB_THREADS) cnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int b0 = blockIdx.x * ROUTE_BLOCK_IDS;
+  const int per = ROUTE_BLOCK_IDS / RB_WAVES;
+  const int beg = min(M, b0 + w * per), end = min(M, beg + per);
+  wave_count(ids, beg, end, E, id_bits(E), lanes_below(lane), lane, cnt[w]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += RB_THREADS) {
+    int c = 0;
+#pragma unroll
+    for (int v = 0; v < RB_WAVES; ++v) c += cnt[v][e];
+    counts[(size_t)blockIdx.x * E + e] = c;
   }
 }
+
+// Step 2 (one workgroup): counts[b][e] -> first routed row of block b's
+// ids of expert e; offsets.
+__global__ __launch_bounds__(ROUTE_THREADS) void route_scan_kernel(int *counts, int nb, int E,
+                                                                   int32_t *offsets) {
+  __shared__ int tot[MOESQ_MAX_EXPERTS + 1];
+  __shared__ int wave_tot[ROUTE_WAVES];
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = counts[(size_t)b * E + e];
+      counts[(size_t)b * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan<ROUTE_THREADS>(tot, E, wave_tot);
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
+    const int o = tot[e];
+    offsets[e] = o;
+    for (int b = 0; b < nb; ++b) counts[(size_t)b * E + e] += o;
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+// Step 3: ranks inside block b on top of its bases; perm and inv_perm.
+__global__ __launch_bounds__(RB_THREADS) void route_scatter_kernel(
+    const int32_t *__restrict__ ids, int M, int E, const int *bases, int32_t *perm,
+    int32_t *inv_perm) {
+  __shared__ int cnt[RB_WAVES][MOESQ_MAX_EXPERTS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nbits = id_bits(E);
+  const uint64_t lt_mask = lanes_below(lane);
+  for (int i = threadIdx.x; i < RB_WAVES * E; i += RB_THREADS) cnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int b0 = blockIdx.x * ROUTE_BLOCK_IDS;
+  const int per = ROUTE_BLOCK_IDS / RB_WAVES;
+  const int beg = min(M, b0 + w * per), end = min(M, beg + per);
+  wave_count(ids, beg, end, E, nbits, lt_mask, lane, cnt[w]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += RB_THREADS) {
+    int run = bases[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int v = 0; v < RB_WAVES; ++v) {
+      const int c = cnt[v][e];
+      cnt[v][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  wave_scatter(ids, beg, end, E, nbits, lt_mask, lane, cnt[w], perm, inv_perm);
+}
+
+static long long route_blocks(long long M) { return (M + ROUTE_BLOCK_IDS - 1) / ROUTE_BLOCK_IDS; }
 
 }  // namespace moesq
 
 using namespace moesq;
 
-extern "C" size_t moesq_route_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+// Inputs up to this many ids take the one-workgroup path.
+constexpr long long ROUTE_SMALL = 4096;
+
+extern "C" size_t moesq_route_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  const long long M = (long long)T * k;
+  if (T < 0 || k < 1 || E < 1 || M <= ROUTE_SMALL) return 0;
+  return (size_t)(route_blocks(M) * E * sizeof(int));
+}
 
 extern "C" moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                                       int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
                                       void *ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   clear_error();
   if (E < 1 || E > MOESQ_MAX_EXPERTS)
     return fail(MOESQ_ERR_SHAPE, "moesq_route: E must be in [1, " +
@@ -160,7 +272,20 @@ extern "C" moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_
   if (!expert_offsets) return fail(MOESQ_ERR_NULL, "moesq_route: expert_offsets is NULL");
   if (M > 0 && (!topk_ids || !perm || !inv_perm))
     return fail(MOESQ_ERR_NULL, "moesq_route: topk_ids, perm and inv_perm must be non-NULL");
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, topk_ids, (int)M, E,
-                     expert_offsets, perm, inv_perm);
+  const size_t need = moesq_route_workspace_bytes(T, k, E);
+  if (need == 0 || !ws || ws_bytes < need) {
+    // one workgroup: no workspace needed (slower for large inputs)
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, topk_ids, (int)M, E,
+                       expert_offsets, perm, inv_perm);
+    return launch_status("moesq_route");
+  }
+  const int nb = (int)route_blocks(M);
+  int *counts = static_cast<int *>(ws);
+  hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids, (int)M,
+                     E, counts);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, counts, nb, E,
+                     expert_offsets);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids,
+                     (int)M, E, counts, perm, inv_perm);
   return launch_status("moesq_route");
 }

@@ -473,8 +473,8 @@ static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_
   const int out_rows = swiglu ? a.N / 2 : a.N;
   const bool small = (long long)a.M < 16ll * a.E || out_rows % 32 != 0;
   if (small)
-    return swiglu ? launch_one<8, 16, 4, 2, 256, true, TILED>(a, stream)
-                  : launch_one<8, 16, 4, 2, 256, false, TILED>(a, stream);
+    return swiglu ? launch_one<8, 16, 2, 2, 256, true, TILED>(a, stream)
+                  : launch_one<8, 16, 2, 2, 256, false, TILED>(a, stream);
   return swiglu ? launch_one<8, 32, 2, 4, 128, true, TILED>(a, stream)
                 : launch_one<8, 32, 2, 4, 128, false, TILED>(a, stream);
 }

@@ -206,7 +206,9 @@ def route(topk_ids, E: int, k: int, stream=None):
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(M, dtype=torch.int32, device=dev)
     inv = torch.empty(M, dtype=torch.int32, device=dev)
-    moesq_route(topk_ids, M // k, k, E, off, perm, inv, None, stream)
+    nws = moesq_route_workspace_bytes(M // k, k, E)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    moesq_route(topk_ids, M // k, k, E, off, perm, inv, ws, stream)
     return off, perm, inv
 
 

@@ -160,9 +160,28 @@ def test_route_edges(lib, E, M, k, mode):
         assert np.array_equal(a, b)
 
 
-def test_route_invalid_ids(lib):
+@pytest.mark.parametrize("E,M", [(384, 65536), (1024, 70001), (7, 5000)])
+def test_route_single_workgroup_path(lib, E, M):
+    """Without workspace, large inputs take the one-workgroup path."""
+    rng = np.random.default_rng(M)
+    ids = rng.integers(0, E, M).astype(np.int32)
+    d = torch.from_numpy(ids).cuda()
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(M, dtype=torch.int32, device="cuda")
+    inv = torch.empty(M, dtype=torch.int32, device="cuda")
+    lib.moesq_route(d, M, 1, E, off, perm, inv, None)
+    torch.cuda.synchronize()
+    ref = oracle.route(ids, E)
+    for a, b in zip((off, perm, inv), ref):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+@pytest.mark.parametrize("big", [False, True])
+def test_route_invalid_ids(lib, big):
     E, k = 6, 2
     ids = np.array([0, 5, -1, 3, 6, 3, 1000, 0, 2, 5], np.int32)
+    if big:
+        ids = np.tile(ids, 1000)
     off, perm, inv = _gpu_route(lib, ids, E, k)
     valid = (ids >= 0) & (ids < E)
     vidx = np.nonzero(valid)[0]

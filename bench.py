@@ -23,6 +23,7 @@ workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -159,6 +160,24 @@ class Step:
         return out
 
 
+def measured_traffic(workload, proj_name):
+    """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
+    counter summary, or None when the GEMM source has changed since the
+    counters were taken (or no summary covers this workload)."""
+    path = os.path.join(ROOT, "profiles", "spgemm_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    csrc = os.path.join(ROOT, "sparse_fp4_expert_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in ("spgemm.hip", "common.hpp"))
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    k = rec.get("kernels", {}).get(f"{workload}/{proj_name}")
+    return None if k is None else k.get("traffic_bytes")
+
+
 def gemm_work(wl, ids):
     """Dense-equivalent flops and compressed weight bytes of the active
     experts, per projection."""
@@ -261,7 +280,7 @@ def main():
         roof = {"bound": "hbm", "achieved": b0 / (g0_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name, wl.proj[0][0])
     roof["kernel"] = f"moesq_grouped_spgemm ({wl.proj[0][0]})"
     roof["kernel_ms"] = g0_ms
 

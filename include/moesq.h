@@ -156,7 +156,7 @@ moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, 
  *   ws, ws_bytes    workspace; moesq_spgemm_workspace_bytes() bytes (may be 0)
  * Rows of y outside every expert range are not written.
  * Limits: K % 32 == 0, N % 16 == 0 (SWIGLU: N % 32 == 0), E <= MOESQ_MAX_EXPERTS,
- *         M >= 0.
+ *         M >= 0, N*K/4 < 2^31 (one expert's values under 2 GiB).
  */
 moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed, const int32_t *expert_offsets,
                                     int32_t M, const moesq_weights_t *w, int32_t epilogue,

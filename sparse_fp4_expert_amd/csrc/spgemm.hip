@@ -45,6 +45,8 @@ struct SpgemmArgs {
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int MS>
 struct Mfma;
@@ -135,6 +137,29 @@ __device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb
   }
 }
 
+// Tiled layout: a lane group's 64 positions of one fragment are 16 value
+// bytes, 8 mask bytes and 2 scale bytes at offsets lo, lo/2, lo/8 past the
+// fragment's segment-row start fv/fm/fs inside the expert's arrays.  Buffer
+// loads take lo in a VGPR and the fragment offset in an SGPR.
+template <int RF>
+__device__ __forceinline__ void load_wchunk_tiled(WChunk<RF, 64> &w, __amdgpu_buffer_rsrc_t vr,
+                                                  __amdgpu_buffer_rsrc_t mr, __amdgpu_buffer_rsrc_t sr,
+                                                  const uint32_t (&fv)[RF], const uint32_t (&fm)[RF],
+                                                  const uint32_t (&fs)[RF], uint32_t lo) {
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vr, lo, fv[f], 0);
+    const u32x2_t m = __builtin_amdgcn_raw_buffer_load_b64(mr, lo >> 1, fm[f], 0);
+    w.v[f][0] = v[0];
+    w.v[f][1] = v[1];
+    w.v[f][2] = v[2];
+    w.v[f][3] = v[3];
+    w.m[f][0] = m[0];
+    w.m[f][1] = m[1];
+    w.s[f] = __builtin_amdgcn_raw_buffer_load_b16(sr, lo >> 3, fs[f], 0);
+  }
+}
+
 template <int RF, int KQ>
 __device__ __forceinline__ void decode_step(uint4 (&A)[RF], const WChunk<RF, KQ> &w,
                                             const float (&sf)[RF][KQ / 32], const uint4 *lut,
@@ -161,11 +186,18 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
   constexpr int KQ = KC * MS / 64;
   constexpr int S = KQ / 8;
   constexpr int UPR = KC / 8;
+  // block scales: the hardware E4M3 (OCP) conversion is exact
   float sf[RF][KQ / 32];
 #pragma unroll
-  for (int f = 0; f < RF; ++f)
-#pragma unroll
-    for (int b = 0; b < KQ / 32; ++b) sf[f][b] = e4m3_to_f32((w.s[f] >> (8 * b)) & 0xffu);
+  for (int f = 0; f < RF; ++f) {
+    if constexpr (KQ == 64) {
+      const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.s[f], 1.0f, false);
+      sf[f][0] = p[0];
+      sf[f][1] = p[1];
+    } else {
+      sf[f][0] = __builtin_amdgcn_cvt_f32_fp8(w.s[f], 0);
+    }
+  }
   const uint16_t *brow = tk + rl * KC;
   const int cbase = (KQ / 8) * q;
   uint4 A[2][RF];
@@ -190,7 +222,9 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
 
 template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, bool TILED>
 __global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void spgemm_kernel(
+// 16-row tiles stream weights: at most 128 VGPRs, so that two 8-wave
+// workgroups share a CU.  32-row tiles hold 128 accumulators per lane.
+__attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void spgemm_kernel(
     SpgemmArgs a) {
   using MF = Mfma<MS>;
   constexpr int LG = 64 / MS;          // lane groups
@@ -209,7 +243,8 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
   __shared__ uint4 lut[256];
   __shared__ int s_lo[MOESQ_MAX_EXPERTS + 1];
   __shared__ int s_item[MOESQ_MAX_EXPERTS + 1];
-  __shared__ __attribute__((aligned(1024))) uint16_t tok[2][BM * KC];
+  __shared__ __attribute__((aligned(1024))) uint16_t tkA[BM * KC];
+  __shared__ __attribute__((aligned(1024))) uint16_t tkB[BM * KC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,6 +328,10 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
     const size_t erow = (size_t)e * N;
     const uint8_t *vb = a.values + erow * vrow, *mb = a.masks + erow * mrow,
                   *sb = a.scales + erow * srow;
+    const uint32_t ebytes = (uint32_t)(vrow * (size_t)N);   // value bytes of one expert
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, (int)ebytes, 0x20000);
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc((void *)mb, 0, (int)(ebytes >> 1), 0x20000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void *)sb, 0, (int)(ebytes >> 3), 0x20000);
     uint32_t fv[RF], fm[RF], fs[RF];
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
@@ -329,9 +368,11 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
     // repeat the last 8; their products only reach unstored outputs or meet
     // zero weights.
     const uint16_t *xb = a.x + (size_t)tok0 * K;
+    const int nrows = nft * MS;
     auto load_tok = [&](uint16_t *buf, int k0) {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
+        if ((wave * BPW + j) * (64 / UPR) >= nrows) break;   // fragment never read
         const int row = (wave * BPW + j) * (64 / UPR) + lane / UPR;
         const int c = (lane % UPR) ^ (row % UPR);
         const int kk = min(k0 + c * 8, K - 8);
@@ -340,6 +381,11 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
             (__attribute__((address_space(1))) void *)(xb + off),
             (__attribute__((address_space(3))) void *)(buf + (wave * BPW + j) * 512), 16, 0, 0);
       }
+    };
+    // tiled: this lane's segment of the chunk at k0, clamped into K
+    auto tlo = [&](int k0) {
+      const uint32_t seg = min((uint32_t)(k0 >> 6) + (uint32_t)q, segs - 1u);
+      return seg * 512u + (uint32_t)rl * 16u;
     };
     auto wok = [&](int k0, bool (&ok)[RF]) {
 #pragma unroll
@@ -360,32 +406,48 @@ __attribute__((amdgpu_waves_per_eu(1, RF * TF * MS / 16 >= 64 ? 1 : 2))) void sp
   #pragma unroll
           for (int i = 0; i < MF::NC; ++i) acc[f][t][i] = 0.f;
 
-      WChunk<RF, KQ> wc;
-      {
-        bool ok[RF];
-        const bool whole = wok(0, ok);
-        uint32_t kv, km, ks;
-        koff(0, kv, km, ks);
-        load_wchunk(wc, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
-        load_tok(tok[0], 0);
-      }
+      auto load_w = [&](WChunk<RF, KQ> &w, int k0) {
+        if constexpr (TILED) {
+          load_wchunk_tiled(w, vr, mr, sr, fv, fm, fs, tlo(k0));
+        } else {
+          bool ok[RF];
+          const bool whole = wok(k0, ok);
+          uint32_t kv, km, ks;
+          koff(k0, kv, km, ks);
+          load_wchunk(w, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
+        }
+      };
+      WChunk<RF, KQ> wA, wB;
+      load_w(wA, 0);
+      load_tok(tkA, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      for (int c = 0; c < nk; ++c) {
-        const bool more = c + 1 < nk;
-        WChunk<RF, KQ> wn;
-        if (more) {
-          bool ok[RF];
-          const bool whole = wok((c + 1) * KC, ok);
-          uint32_t kv, km, ks;
-          koff((c + 1) * KC, kv, km, ks);
-          load_wchunk(wn, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
-          load_tok(tok[(c + 1) & 1], (c + 1) * KC);
+      // One chunk: prefetch chunk c + 1 into (nxt, wn), compute chunk c from
+      // (cur, wc).  The two token buffers are distinct LDS objects, so the
+      // reads of `cur` need not wait for the direct-to-LDS loads into `nxt`.
+      auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, WChunk<RF, KQ> &wc,
+                       WChunk<RF, KQ> &wn) {
+        if (c + 1 < nk) {
+          load_w(wn, (c + 1) * KC);
+          load_tok(nxt, (c + 1) * KC);
         }
-        mma_chunk<MS, RF, TF, KC, FULL>(acc, tok[c & 1], wc, lut, nft, q, rl);
+        if constexpr (TILED) {
+          if ((c + 1) * KC > K) {
+            // segments past K were clamped to the last one: clear their masks
+            const bool ok = (uint32_t)((c * KC) >> 6) + (uint32_t)q < segs;
+#pragma unroll
+            for (int f = 0; f < RF; ++f)
+#pragma unroll
+              for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) wc.m[f][i] = ok ? wc.m[f][i] : 0u;
+          }
+        }
+        mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (more) wc = wn;
+      };
+      for (int c = 0; c < nk; c += 2) {
+        chunk(c, tkA, tkB, wA, wB);
+        if (c + 1 < nk) chunk(c + 1, tkB, tkA, wB, wA);
       }
 
       // Epilogue.  Accumulator element r of a lane holds weight row
@@ -499,6 +561,8 @@ static moesq_status_t check_weights(const moesq_weights_t *w, const char *who) {
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": N must be a positive multiple of 16");
   if (w->K < 32 || w->K % 32)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": K must be a positive multiple of 32");
+  if ((long long)w->N * w->K / 4 > 0x7fffffffll)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": one expert's value array must stay under 2 GiB");
   return MOESQ_OK;
 }
 

@@ -85,6 +85,8 @@ def test_spgemm_rejects(m):
     assert g(0x10, ok_off, 4, ref(_desc(m, E=0)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
     assert g(0x10, ok_off, 4, ref(_desc(m, E=1025)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
     assert g(0x10, ok_off, 4, ref(_desc(m, N=48)), 1, 0x10, None, 0, None) == m.ERR_SHAPE  # SwiGLU N%32
+    big = _desc(m, N=1 << 16, K=1 << 17)                       # one expert's values = 2 GiB
+    assert g(0x10, ok_off, 4, ref(big), 0, 0x10, None, 0, None) == m.ERR_SHAPE
     assert g(0x10, ok_off, 4, ref(_desc(m)), 5, 0x10, None, 0, None) == m.ERR_ARG          # epilogue
     assert g(0x10, None, 4, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_NULL
     assert g(0x10, ok_off, -1, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_SHAPE

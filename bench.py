@@ -9,9 +9,11 @@ device-resident input:
   (down) -> router-weighted combine            (trillion-class workloads)
   route -> permute -> grouped GEMM -> combine  (30B-class workloads)
 Inputs (tokens, top-k ids, router weights, packed expert weights) are built
-and packed on the GPU before timing.  The timed region is bracketed by a
-device synchronisation on both sides; per-kernel durations come from HIP
-events recorded on the stream the kernels run on.
+and packed on the GPU before timing.  Every step replays a HIP graph of its
+launches; the timed region is bracketed by a device synchronisation on both
+sides.  Per-kernel durations come from HIP events recorded on the launch
+stream around a graph of back-to-back launches of that kernel alone, with
+the weight replicas rotating as in the steps.
 
 Prints one JSON line.  value = dense-equivalent GEMM TFLOP/s of the whole
 step (2*M*N*K summed over the projections, divided by the step time) for
@@ -128,9 +130,11 @@ class Step:
         self.out = torch.empty(T if wl.weighted_combine else M, self.y.shape[1], **bf)
         self.names = ["route", "permute"] + [f"gemm_{p[0]}" for p in wl.proj] + ["combine"]
 
-    def run(self, timed=False):
+    def calls(self):
+        """(name, launch) of every kernel of one step, on the next weight
+        replica."""
         m, wl = self.m, self.wl
-        self.w = self.replicas[self.turn % len(self.replicas)]
+        w = self.replicas[self.turn % len(self.replicas)]
         self.turn += 1
         calls = [
             lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm, self.inv,
@@ -138,26 +142,57 @@ class Step:
             lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr),
         ]
         if wl.swiglu:
-            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, self.w[0],
+            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, w[0],
                                                         m.EPI_SWIGLU, self.h))
-            calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, self.w[1],
+            calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, w[1],
                                                         m.EPI_NONE, self.y))
         else:
-            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, self.w[0],
+            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, w[0],
                                                         m.EPI_NONE, self.y))
         tw = self.tw if wl.weighted_combine else None
         calls.append(lambda: m.moesq_unpermute(self.y, self.inv, tw, wl.T, wl.k,
                                                self.y.shape[1], self.out))
-        out = []
-        for c in calls:
-            if timed:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record()
+        return list(zip(self.names, calls))
+
+    def run(self):
+        for _, c in self.calls():
             c()
-            if timed:
-                ev[1].record()
-                out.append(ev)
-        return out
+
+    def capture_steps(self):
+        """One HIP graph of the whole step per weight replica (the graph
+        holds that replica's weight pointers)."""
+        graphs = []
+        for _ in range(len(self.replicas)):
+            g = torch.cuda.CUDAGraph()
+            launches = self.calls()
+            with torch.cuda.graph(g):
+                for _, c in launches:
+                    c()
+            graphs.append(g)
+        return graphs
+
+    def kernel_ms(self, reps):
+        """Average duration of each kernel of the step: HIP events on the
+        launch stream around a graph of `reps` back-to-back launches of that
+        kernel alone (weight replicas rotating), replayed twice."""
+        res = {}
+        n = len(self.names)
+        for i in range(n):
+            g = torch.cuda.CUDAGraph()
+            launches = [self.calls()[i][1] for _ in range(reps)]
+            with torch.cuda.graph(g):
+                for c in launches:
+                    c()
+            g.replay()
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
+            g.replay()
+            g.replay()
+            ev[1].record()
+            torch.cuda.synchronize()
+            res[self.names[i]] = ev[0].elapsed_time(ev[1]) / (2 * reps)
+            del g
+        return res
 
 
 def measured_traffic(workload, proj_name):
@@ -251,16 +286,20 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps, synchronised on both sides.  The
-    # per-kernel HIP events are recorded on the launch stream inside it.
+    # Each step replays a HIP graph of its five or six launches, so that
+    # short decode kernels are not separated by host launch gaps.
+    graphs = step.capture_steps()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    # Timed region: exactly `steps` steps, synchronised on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    events = [step.run(timed=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    kernel_ms = {n: sum(ev[i][0].elapsed_time(ev[i][1]) for ev in events) / args.steps
-                 for i, n in enumerate(step.names)}
+    kernel_ms = step.kernel_ms(reps=max(8, len(step.replicas)))
 
     work, active = gemm_work(wl, step.ids_host)
     total_flops = sum(f for f, _ in work)

@@ -25,7 +25,8 @@
  *     passed as uint16_t (raw bf16 bits).  All tensors are dense row-major.
  *   - The caller owns every buffer.  The library allocates and frees no
  *     device memory, never synchronises the stream, and enqueues all work on
- *     `stream` (0 = the null stream).
+ *     `stream` (0 = the null stream).  (Exception: the debug call
+ *     moesq_validate.)
  *   - A call checks its arguments on the host first; on a bad argument it
  *     returns an error and launches nothing.  A failed launch returns
  *     MOESQ_ERR_HIP.  moesq_last_error() gives a detail string for the last
@@ -212,6 +213,30 @@ moesq_status_t moesq_tile_weights(const moesq_weights_t *src, uint8_t *values, u
  */
 moesq_status_t moesq_decode_weights(const moesq_weights_t *w, int32_t expert, uint16_t *dense,
                                     hipStream_t stream);
+
+/*
+ * DEBUG check of the caller contracts that the kernels above rely on without
+ * checking them ("A Sparse-quantized representation": four kept values per
+ * group of eight, E4M3 block scales).  Unlike every other call it allocates a
+ * small device buffer (40 bytes), enqueues its checks on `stream` and
+ * SYNCHRONISES the stream; it is not for the hot path.  Each input may be NULL
+ * (w too) to skip its checks.
+ *   topk_ids [T*k]     every id in [0, E)
+ *   expert_offsets [E+1] offsets[0] == 0, non-decreasing, offsets[E] == T*k
+ *   w (host struct)    every mask byte has exactly four bits set; every
+ *                      scale byte is a non-negative finite E4M3 code (not
+ *                      0x7F, sign bit clear); every global scale is finite
+ *                      and >= 0.  Either layout (the checks are per byte).
+ *   counts (host, may be NULL) [5] out: violations of the five checks, in
+ *                      the order ids, offsets, masks, scales, global scales.
+ * Returns MOESQ_OK when every check passes, MOESQ_ERR_ARG when one fails
+ * (moesq_last_error() names the failed checks and their counts), and the
+ * usual errors for bad sizes or a failed HIP call.
+ * Limits: with ids or offsets, 1 <= E <= MOESQ_MAX_EXPERTS, T >= 0, k >= 1.
+ */
+moesq_status_t moesq_validate(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                              const int32_t *expert_offsets, const moesq_weights_t *w,
+                              uint64_t *counts, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char *moesq_status_string(moesq_status_t st);

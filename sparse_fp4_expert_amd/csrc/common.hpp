@@ -41,9 +41,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// E4M3 code (sign ignored: block scales are non-negative) -> fp32, exact.
-// Exponent field 0 is subnormal (m * 2^-9); 0x7F (NaN) never comes out of
-// the packer and decodes here as 480, a finite value.
+// E4M3 code (sign ignored) -> fp32, exact; used by the packer on the codes it
+// has just encoded (never 0x7F or negative).  Exponent field 0 is subnormal
+// (m * 2^-9).  The decoders use the hardware conversion instead.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float sub = (float)m * 0.001953125f;                       // m * 2^-9

@@ -183,7 +183,8 @@ __global__ __launch_bounds__(PACK_THREADS) void decode_kernel(
     so = G >> 2;
   }
   const uint32_t v = *reinterpret_cast<const uint16_t *>(values + vo);
-  const float s = e4m3_to_f32(scales[so]);
+  // the GEMM's scale conversion (hardware OCP E4M3), so both agree on any byte
+  const float s = __builtin_amdgcn_cvt_f32_fp8(scales[so], 0);
   dense[G] = decode_group<0>(masks[mo], v, s, lut);
 }
 

@@ -53,6 +53,8 @@ _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
 _tile = _sig("moesq_tile_weights", _i32, ctypes.POINTER(WeightsDesc), _vp, _vp, _vp, _vp)
+_validate = _sig("moesq_validate", _i32, _vp, _i32, _i32, _i32, _vp, ctypes.POINTER(WeightsDesc),
+                 ctypes.POINTER(ctypes.c_uint64), _vp)
 _status_string = _sig("moesq_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moesq_last_error", ctypes.c_char_p)
 _version = _sig("moesq_version", _i32)
@@ -60,7 +62,7 @@ _version = _sig("moesq_version", _i32)
 EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes", "moesq_unpermute",
             "moesq_pack_weights", "moesq_tile_weights", "moesq_decode_weights",
-            "moesq_status_string",
+            "moesq_validate", "moesq_status_string",
             "moesq_last_error", "moesq_version"]
 
 
@@ -195,6 +197,23 @@ def moesq_tile_weights(src: Weights, values, masks, scales, stream=None):
 def moesq_decode_weights(w: Weights, expert: int, dense, stream=None):
     _check(_decode(ctypes.byref(w.desc), expert, _ptr(dense, torch.bfloat16, "dense"),
                    _stream(stream)))
+
+
+VALIDATE_CHECKS = ("ids", "offsets", "masks", "scales", "global_scales")
+
+
+def moesq_validate(topk_ids=None, T: int = 0, k: int = 1, E: int = 1, expert_offsets=None,
+                   w: Weights | None = None, stream=None) -> dict:
+    """Debug check of the caller contracts (synchronises).  Returns the
+    violation count of each check; a failed check is not an exception (the
+    counts say which), bad sizes and HIP failures are."""
+    counts = (ctypes.c_uint64 * len(VALIDATE_CHECKS))()
+    st = _validate(_ptr(topk_ids, torch.int32, "topk_ids", True), T, k, E,
+                   _ptr(expert_offsets, torch.int32, "expert_offsets", True),
+                   None if w is None else ctypes.byref(w.desc), counts, _stream(stream))
+    if st != ERR_ARG:
+        _check(st)
+    return dict(zip(VALIDATE_CHECKS, (int(c) for c in counts)))
 
 
 # ------------------------------------------------------------ helpers (allocate with torch)

@@ -103,3 +103,15 @@ def test_pack_and_decode_reject(m):
     assert m._decode(ctypes.byref(d), -1, 0x10, None) == m.ERR_ARG
     assert m._decode(ctypes.byref(d), 0, None, None) == m.ERR_NULL
     assert m._decode(None, 0, 0x10, None) == m.ERR_NULL
+
+
+def test_validate_rejects(m):
+    v = m._validate
+    ref = ctypes.byref
+    assert v(0x10, 4, 2, 0, None, None, None, None) == m.ERR_SHAPE        # E = 0 with ids
+    assert v(0x10, 4, 2, 2000, None, None, None, None) == m.ERR_SHAPE     # E too large
+    assert v(None, -1, 2, 8, 0x10, None, None, None) == m.ERR_SHAPE       # T < 0 with offsets
+    assert v(None, 4, 0, 8, 0x10, None, None, None) == m.ERR_SHAPE        # k < 1
+    assert v(None, 0, 1, 1, None, ref(_desc(m, layout=7)), None, None) == m.ERR_LAYOUT
+    assert v(None, 0, 1, 1, None, ref(_desc(m, null=True)), None, None) == m.ERR_NULL
+    assert v(None, 0, 1, 1, None, ref(_desc(m, K=48)), None, None) == m.ERR_SHAPE

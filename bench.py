@@ -1,7 +1,7 @@
 """Throughput of the grouped 4:8 sparse-FP4 expert path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--sweep]
 
 One step is one pass of the whole hot path over one batch of synthetic,
 device-resident input:
@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of steps: time the first grouped GEMM of --workload over a grid "
+                         "of active-expert counts G x rows per expert R (one JSON line per point)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain gather copy of known size (moesq_unpermute without "
                          "weights over 512 MiB in, 512 MiB out) to scale HBM byte counters")
@@ -195,6 +198,58 @@ class Step:
         return res
 
 
+def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launches=16):
+    """Grouped GEMM of the workload's first projection (plain epilogue) over
+    G active experts with R routed rows each, as the pages sweep expert-group
+    count x rows per expert.  Each launch reads a different window of G
+    experts (and weight replicas rotate when the whole set is under 1 GiB),
+    so weights come from HBM; times are HIP events around a graph of
+    `launches` back-to-back launches."""
+    _, N, K = wl.proj[0]
+    dev = torch.device("cuda")
+    w0 = pack_on_gpu(m, wl, 0)
+    reps = [w0] + [m.Weights(w0.values.clone(), w0.masks.clone(), w0.scales.clone(),
+                             w0.global_scale.clone(), w0.layout)
+                   for _ in range(max(0, -(-ROTATE_BYTES // w0.nbytes) - 1))]
+    gen = torch.Generator(device="cpu").manual_seed(wl.seed + 77)
+    for G in Gs:
+        if G > wl.E:
+            continue
+        for R in Rs:
+            M = G * R
+            x = (torch.randn(M, K, generator=gen) * 1.0).to(torch.bfloat16).to(dev)
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            offs = []
+            for i in range(launches):
+                start = (i // len(reps)) * G % wl.E
+                counts = np.zeros(wl.E, np.int64)
+                counts[(start + np.arange(G)) % wl.E] = R
+                offs.append(torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev))
+            calls = [(lambda o=offs[i], w=reps[i % len(reps)]:
+                      m.moesq_grouped_spgemm(x, o, M, w, m.EPI_NONE, y)) for i in range(launches)]
+            for c in calls[:2]:
+                c()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in calls:
+                    c()
+            g.replay()
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
+            g.replay()
+            ev[1].record()
+            torch.cuda.synchronize()
+            us = 1e3 * ev[0].elapsed_time(ev[1]) / launches
+            wbytes = G * (N * K * 13 // 32 + 4)
+            print(json.dumps({"sweep": wl.name, "N": N, "K": K, "G": G, "R": R, "M": M,
+                              "kernel_us": round(us, 2),
+                              "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
+                              "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
+                              "tflops_dense_eq": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
+                              "weight_replicas": len(reps)}), flush=True)
+            del g
+
+
 def measured_traffic(workload, proj_name):
     """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
     counter summary, or None when the GEMM source has changed since the
@@ -226,27 +281,59 @@ def gemm_work(wl, ids):
     return res, active
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s):
-    """The CPU oracle on a bounded sample of the same workload: the experts
-    with the most routed rows, each through oracle compression-decode and the
-    float64 GEMM of all its rows (every projection), until the budget is
-    spent.  Reported in the step's unit, scaled by the sampled share."""
+    """The CPU oracle on the same workload, each phase timed on its own.
+
+    Route, permute and the combine run on the whole workload (data movement;
+    the combine reads a zero Y of the right shape).  Decode, the float64 GEMM
+    of every projection and SwiGLU run on the experts with the most routed
+    rows until about `budget_s` seconds are spent, and are scaled to all
+    active experts by their share of the GEMM flops (prefill) or of the
+    compressed weight bytes (decode).  Compressing the dense weights (the
+    packer, untimed on the GPU too) is timed but left out of the total.
+    Returns (work, seconds, threads, sample, phases)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    ids, _ = synth.routing(wl)
+    ids, tw = synth.routing(wl)
     x = synth.tokens(wl).to(torch.float64).numpy()
-    off, perm, _ = oracle.route(ids, wl.E)
+    ph = dict.fromkeys(["route", "permute", "compress", "decode", "gemm", "swiglu", "combine"], 0.0)
+
+    t = time.perf_counter()
+    off, perm, inv = oracle.route(ids, wl.E)
+    ph["route"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.permute(x, perm, wl.k)
+    ph["permute"] = time.perf_counter() - t
+    n_out = wl.proj[-1][1]
+    y_zero = np.zeros((wl.M, n_out), np.float64)
+    t = time.perf_counter()
+    oracle.unpermute(y_zero, inv, tw if wl.weighted_combine else None, wl.T, wl.k)
+    ph["combine"] = time.perf_counter() - t
+    del y_zero
+
     counts = np.diff(off)
+    active = int((counts > 0).sum())
     order = np.argsort(-counts, kind="stable")
+    flops_all = sum(2.0 * wl.M * N * K for _, N, K in wl.proj)
+    bytes_all = sum(active * (N * K * 13 // 32 + 4) for _, N, K in wl.proj)
     t0 = time.perf_counter()
     flops = 0.0
     wbytes = 0
-    rows_done = 0
-    experts = 0
+    rows_done = experts = 0
     for e in order:
         if counts[e] == 0 or time.perf_counter() - t0 > budget_s:
             break
@@ -254,19 +341,33 @@ def cpu_baseline(wl, budget_s):
         a = x[rows]
         for p, (_, N, K) in enumerate(wl.proj):
             dense = synth.dense_expert(wl, p, int(e)).numpy()
+            t = time.perf_counter()
             pk = oracle.quantize(dense)
+            ph["compress"] += time.perf_counter() - t
+            t = time.perf_counter()
             Wd = oracle.decode(pk)
+            ph["decode"] += time.perf_counter() - t
+            t = time.perf_counter()
             y = oracle.expert_gemm(a, Wd)
+            ph["gemm"] += time.perf_counter() - t
             if wl.swiglu and p == 0:
+                t = time.perf_counter()
                 a = oracle.bf16_round(oracle.swiglu(y))
+                ph["swiglu"] += time.perf_counter() - t
             flops += 2.0 * len(rows) * N * K
             wbytes += pk.nbytes
         rows_done += len(rows)
         experts += 1
-    dt = time.perf_counter() - t0
-    sample = (f"{experts} experts with the most rows ({rows_done} of {wl.M} routed rows), "
-              f"each: compress + decode + float64 GEMM of every projection")
-    return flops, wbytes, dt, threads, sample
+    prefill = wl.M >= 4096
+    scale = flops_all / flops if prefill else bytes_all / wbytes
+    total = ph["route"] + ph["permute"] + ph["combine"] + scale * (ph["decode"] + ph["gemm"] + ph["swiglu"])
+    sample = (f"route, permute and combine of all {wl.M} routed rows; decode + float64 GEMM"
+              f"{' + SwiGLU' if wl.swiglu else ''} of the {experts} experts with the most rows "
+              f"({rows_done} rows), scaled x{scale:.1f} to all {active} active experts")
+    phases = {k: round(v, 4) for k, v in ph.items()}
+    phases["scaled_to_all_experts"] = round(scale, 3)
+    work = flops_all if prefill else bytes_all
+    return work, total, threads, sample, phases
 
 
 def main():
@@ -281,6 +382,9 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(m, wl)
+        return
     step = Step(m, wl)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -315,6 +419,15 @@ def main():
     if prefill:
         roof = {"bound": "mfma", "achieved": f0 / (g0_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
+        # MFMAs the kernel executes: each expert's rows padded to whole
+        # 32-row token fragments (the prefill tile); one MAC per kept weight
+        # is the useful rate
+        _, N0, K0 = wl.proj[0]
+        counts = np.bincount(step.ids_host, minlength=wl.E)
+        padded = float((-(-counts // 32) * 32).sum())
+        roof["mfma_executed_tflops"] = 2.0 * padded * N0 * K0 / (g0_ms * 1e-3) / 1e12
+        roof["mfma_executed_frac"] = roof["mfma_executed_tflops"] / PEAK_BF16_TFLOPS
+        roof["useful_tflops"] = 0.5 * roof["achieved"]
     else:
         roof = {"bound": "hbm", "achieved": b0 / (g0_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -335,10 +448,11 @@ def main():
            "weight_gb_active": total_wbytes / 1e9,
            "roofline": roof}
     if not args.no_cpu_baseline:
-        fl, wb, dt, threads, sample = cpu_baseline(wl, args.cpu_seconds)
-        cv = fl / dt / 1e12 if prefill else wb / dt / 1e9
+        work, dt, threads, sample, phases = cpu_baseline(wl, args.cpu_seconds)
+        cv = work / dt / 1e12 if prefill else work / dt / 1e9
         res["cpu_baseline"] = {"value": cv, "unit": unit, "cores": threads, "kind": "oracle",
-                               "sample": sample, "seconds": dt}
+                               "sample": sample, "seconds_full_step": dt, "phases_s": phases,
+                               "cpu": cpu_model()}
     print(json.dumps(res))
 
 

@@ -289,14 +289,18 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   const uint32_t segs = (uint32_t)(K >> 6);
 
   // Items of one round of workgroups are spread XCD-major: the grid is a
-  // multiple of 8 and workgroup b runs on XCD b % 8, so consecutive items
-  // (the row tiles of one token tile) share that XCD's L2.
+  // multiple of 8 and workgroup b runs on XCD b % 8.  A round's n items are
+  // cut into 8 runs of ceil(n/8) consecutive items, one run per XCD, so
+  // consecutive items (the row tiles of one token tile) share an XCD's L2
+  // and a short last round still uses every XCD.
   const int G = gridDim.x;
-  const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
 
   for (int base = 0; base < total; base += G) {
-    const int item = base + slot;
-    if (item >= total) break;
+    const int n_round = min(G, total - base);
+    const int per = (n_round + 7) >> 3;
+    if (wg_in_xcd >= per || xcd * per + wg_in_xcd >= n_round) break;   // no item in the last round
+    const int item = base + xcd * per + wg_in_xcd;
     int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -522,18 +526,19 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   return launch_status("moesq_grouped_spgemm");
 }
 
-// Tile choice.  Few routed rows per expert (decode): 16-token fragments,
-// 32-token tiles, 256-position chunks (wide weight loads), two waves per
-// SIMD -- the kernel streams weights.  Otherwise 32x32x16 MFMAs on 128
-// weight rows x 128 tokens per wave, one wave per SIMD with the 256
-// accumulators in AGPRs, so that every decoded weight feeds 4 MFMAs of
-// 32 tokens.  Fragments are whole: the 32-row variant needs the output
-// rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the 16-row
-// variant runs.
+// Tile choice.  Up to 32 routed rows per expert on average (a sweep over
+// active experts x rows per expert puts the crossover between 32 and 64
+// rows): the streaming tile, 16x16x32 MFMAs on 32 weight rows x 32 tokens
+// per wave, 256-position chunks, four waves per SIMD (two 8-wave workgroups
+// per CU).  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
+// x 128 tokens per wave, two waves per SIMD, so that every decoded weight
+// feeds 4 MFMAs of 32 tokens.  Fragments are whole: the 32-row tile needs
+// the output rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the
+// 16-row tile runs.
 template <bool TILED>
 static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
-  const bool small = (long long)a.M < 16ll * a.E || out_rows % 32 != 0;
+  const bool small = (long long)a.M <= 32ll * a.E || out_rows % 32 != 0;
   if (small)
     return swiglu ? launch_one<8, 16, 2, 2, 256, true, TILED>(a, stream)
                   : launch_one<8, 16, 2, 2, 256, false, TILED>(a, stream);

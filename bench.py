@@ -5,9 +5,11 @@
 
 One step is one pass of the whole hot path over one batch of synthetic,
 device-resident input:
-  route -> permute -> grouped GEMM (gate/up, SwiGLU epilogue) -> grouped GEMM
+  route -> dispatch + grouped GEMM (gate/up, SwiGLU epilogue) -> grouped GEMM
   (down) -> router-weighted combine            (trillion-class workloads)
-  route -> permute -> grouped GEMM -> combine  (30B-class workloads)
+  route -> dispatch + grouped GEMM -> combine  (30B-class workloads)
+The dispatch (gather of the routed token rows) runs inside the first GEMM;
+--unfused runs it as its own permute kernel instead.
 Inputs (tokens, top-k ids, router weights, packed expert weights) are built
 and packed on the GPU before timing.  Every step replays a HIP graph of its
 launches; the timed region is bracketed by a device synchronisation on both
@@ -54,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the dispatch as its own permute kernel instead of inside the first GEMM")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of steps: time the first grouped GEMM of --workload over a grid "
                          "of active-expert counts G x rows per expert R (one JSON line per point)")
@@ -98,8 +102,8 @@ def pack_on_gpu(m, wl, proj, chunk=16):
 class Step:
     """Buffers and launches of one pass of the hot path."""
 
-    def __init__(self, m, wl):
-        self.m, self.wl = m, wl
+    def __init__(self, m, wl, fused=True):
+        self.m, self.wl, self.fused = m, wl, fused
         dev = torch.device("cuda")
         ids, tw = synth.routing(wl)
         self.ids_host = ids
@@ -124,14 +128,15 @@ class Step:
         self.inv = torch.empty(M, **i32)
         nws = m.moesq_route_workspace_bytes(T, k, E)
         self.route_ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
-        self.xr = torch.empty(M, wl.K_in, **bf)
+        self.xr = None if fused else torch.empty(M, wl.K_in, **bf)
         if wl.swiglu:
             self.h = torch.empty(M, wl.proj[0][1] // 2, **bf)
             self.y = torch.empty(M, wl.proj[1][1], **bf)
         else:
             self.y = torch.empty(M, wl.proj[0][1], **bf)
         self.out = torch.empty(T if wl.weighted_combine else M, self.y.shape[1], **bf)
-        self.names = ["route", "permute"] + [f"gemm_{p[0]}" for p in wl.proj] + ["combine"]
+        self.names = (["route"] + ([] if fused else ["permute"]) + [f"gemm_{p[0]}" for p in wl.proj]
+                      + ["combine"])
 
     def calls(self):
         """(name, launch) of every kernel of one step, on the next weight
@@ -142,16 +147,23 @@ class Step:
         calls = [
             lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm, self.inv,
                                   self.route_ws),
-            lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr),
         ]
+        if not self.fused:
+            calls.append(lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr))
+
+        def first(epi, out):
+            # dispatch fused into the first GEMM, or the routed copy
+            if self.fused:
+                return lambda: m.moesq_grouped_spgemm_gather(self.x, self.perm, wl.T, wl.k, self.off,
+                                                             w[0], epi, out)
+            return lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, w[0], epi, out)
+
         if wl.swiglu:
-            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, w[0],
-                                                        m.EPI_SWIGLU, self.h))
+            calls.append(first(m.EPI_SWIGLU, self.h))
             calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, w[1],
                                                         m.EPI_NONE, self.y))
         else:
-            calls.append(lambda: m.moesq_grouped_spgemm(self.xr, self.off, wl.M, w[0],
-                                                        m.EPI_NONE, self.y))
+            calls.append(first(m.EPI_NONE, self.y))
         tw = self.tw if wl.weighted_combine else None
         calls.append(lambda: m.moesq_unpermute(self.y, self.inv, tw, wl.T, wl.k,
                                                self.y.shape[1], self.out))
@@ -385,7 +397,7 @@ def main():
     if args.sweep:
         sweep(m, wl)
         return
-    step = Step(m, wl)
+    step = Step(m, wl, fused=not args.unfused)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -413,7 +425,7 @@ def main():
         value, unit = total_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
     else:
         value, unit = total_wbytes / (ms_step * 1e-3) / 1e9, "GB/s"
-    g0 = step.names[2]
+    g0 = f"gemm_{wl.proj[0][0]}"
     g0_ms = kernel_ms[g0]
     f0, b0 = work[0]
     if prefill:

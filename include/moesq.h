@@ -165,6 +165,23 @@ moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed, const int32_t *exp
 size_t moesq_spgemm_workspace_bytes(int32_t M, const moesq_weights_t *w);
 
 /*
+ * Dispatch fused into the grouped GEMM ("D.1 Implementation details": the
+ * serving kernels fuse dispatch with the expert GEMM): the same result as
+ * moesq_permute(x, perm, T, k, K, x_routed) followed by
+ * moesq_grouped_spgemm(x_routed, expert_offsets, T*k, w, epilogue, y, ...),
+ * without the routed copy of the tokens -- routed row r reads token
+ * perm[r] / k of x directly.
+ *   x        [T][K] bf16 tokens;  perm [T*k] int32 (moesq_route output)
+ *   expert_offsets, w, epilogue, y, ws, ws_bytes: as moesq_grouped_spgemm,
+ *   with M = T*k.  Rows r whose perm[r] is outside [0, T*k) come out zero.
+ * Limits: those of moesq_grouped_spgemm; T >= 0, k >= 1, T*k < 2^31.
+ */
+moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const int32_t *perm, int32_t T,
+                                           int32_t k, const int32_t *expert_offsets,
+                                           const moesq_weights_t *w, int32_t epilogue, uint16_t *y,
+                                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Combine.
  *   topk_weights != NULL: out[t][:] = bf16_rne( sum_{j<k} w[t*k+j] * y[inv_perm[t*k+j]][:] ),
  *                         fp32 accumulation in j order; out is [T][N].

@@ -33,7 +33,9 @@
 namespace moesq {
 
 struct SpgemmArgs {
-  const uint16_t *x;
+  const uint16_t *x;        // routed rows [M][K], or tokens [T][K] with `perm`
+  const int32_t *perm;      // NULL, or gather: routed row r reads token perm[r] / k
+  int T, k;                 // token rows of x and experts per token (gather only)
   const int32_t *offsets;
   const uint8_t *values;
   const uint8_t *masks;
@@ -371,8 +373,22 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     // Rows past the tile repeat the last routed row and positions past K
     // repeat the last 8; their products only reach unstored outputs or meet
     // zero weights.
-    const uint16_t *xb = a.x + (size_t)tok0 * K;
+    // Source row of each token-tile row this lane loads: the routed row, or
+    // with a gather permutation the token perm[routed row] / k (dispatch
+    // fused into the GEMM; an out-of-range entry reads token 0 and its
+    // output row is written as zero, as a zero routed row would give).
     const int nrows = nft * MS;
+    const uint16_t *srow[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int r = tok0 + min((wave * BPW + j) * (64 / UPR) + lane / UPR, ntok - 1);
+      int src = r;
+      if (a.perm) {
+        const int pi = a.perm[r];
+        src = (pi >= 0 && pi < a.T * a.k) ? pi / a.k : 0;
+      }
+      srow[j] = a.x + (size_t)src * K;
+    }
     auto load_tok = [&](uint16_t *buf, int k0) {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
@@ -380,9 +396,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         const int row = (wave * BPW + j) * (64 / UPR) + lane / UPR;
         const int c = (lane % UPR) ^ (row % UPR);
         const int kk = min(k0 + c * 8, K - 8);
-        const uint32_t off = (uint32_t)min(row, ntok - 1) * (uint32_t)K + (uint32_t)kk;
         __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void *)(xb + off),
+            (__attribute__((address_space(1))) void *)(srow[j] + kk),
             (__attribute__((address_space(3))) void *)(buf + (wave * BPW + j) * 512), 16, 0, 0);
       }
     };
@@ -463,6 +478,11 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         const int trow = t * MS + rl;
         if (trow >= ntok) continue;
         const size_t out_r = (size_t)(tok0 + trow);
+        bool keep = true;
+        if (a.perm) {
+          const int pi = a.perm[out_r];
+          keep = pi >= 0 && pi < a.T * a.k;
+        }
   #pragma unroll
         for (int r4 = 0; r4 < MF::NC / 4; ++r4) {
           const int roff = r4 * 4 * LG + 4 * q;
@@ -472,8 +492,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
               if (!fval[f]) continue;
               const typename MF::C &c = acc[f][t];
               uint2 o;
-              o.x = pack_bf16x2(g * c[4 * r4 + 0], g * c[4 * r4 + 1]);
-              o.y = pack_bf16x2(g * c[4 * r4 + 2], g * c[4 * r4 + 3]);
+              o.x = keep ? pack_bf16x2(g * c[4 * r4 + 0], g * c[4 * r4 + 1]) : 0u;
+              o.y = keep ? pack_bf16x2(g * c[4 * r4 + 2], g * c[4 * r4 + 3]) : 0u;
               *reinterpret_cast<uint2 *>(a.y + out_r * N + (frow[f] + roff)) = o;
             }
           } else {
@@ -485,8 +505,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   #pragma unroll
               for (int i = 0; i < 4; ++i) h[i] = silu_f32(g * gt[4 * r4 + i]) * (g * up[4 * r4 + i]);
               uint2 o;
-              o.x = pack_bf16x2(h[0], h[1]);
-              o.y = pack_bf16x2(h[2], h[3]);
+              o.x = keep ? pack_bf16x2(h[0], h[1]) : 0u;
+              o.y = keep ? pack_bf16x2(h[2], h[3]) : 0u;
               *reinterpret_cast<uint2 *>(a.y + out_r * half + (frow[f] + roff)) = o;
             }
           }
@@ -577,26 +597,26 @@ using namespace moesq;
 
 extern "C" size_t moesq_spgemm_workspace_bytes(int32_t, const moesq_weights_t *) { return 0; }
 
-extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
-                                               const int32_t *expert_offsets, int32_t M,
-                                               const moesq_weights_t *w, int32_t epilogue,
-                                               uint16_t *y, void *ws, size_t ws_bytes,
-                                               hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int32_t *perm, int32_t T,
+                                   int32_t k, const int32_t *expert_offsets, int32_t M,
+                                   const moesq_weights_t *w, int32_t epilogue, uint16_t *y,
+                                   hipStream_t stream) {
   clear_error();
-  moesq_status_t st = check_weights(w, "moesq_grouped_spgemm");
+  moesq_status_t st = check_weights(w, who);
   if (st != MOESQ_OK) return st;
   if (epilogue != MOESQ_EPI_NONE && epilogue != MOESQ_EPI_SWIGLU)
-    return fail(MOESQ_ERR_ARG, "moesq_grouped_spgemm: unknown epilogue");
+    return fail(MOESQ_ERR_ARG, std::string(who) + ": unknown epilogue");
   if (epilogue == MOESQ_EPI_SWIGLU && w->N % 32)
-    return fail(MOESQ_ERR_SHAPE, "moesq_grouped_spgemm: SwiGLU needs N % 32 == 0");
-  if (M < 0) return fail(MOESQ_ERR_SHAPE, "moesq_grouped_spgemm: M must be >= 0");
-  if (!expert_offsets) return fail(MOESQ_ERR_NULL, "moesq_grouped_spgemm: expert_offsets is NULL");
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": SwiGLU needs N % 32 == 0");
+  if (M < 0) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": M must be >= 0");
+  if (!expert_offsets) return fail(MOESQ_ERR_NULL, std::string(who) + ": expert_offsets is NULL");
   if (M == 0) return MOESQ_OK;
-  if (!x_routed || !y) return fail(MOESQ_ERR_NULL, "moesq_grouped_spgemm: NULL x_routed or y");
+  if (!x || !y) return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL input or output rows");
   SpgemmArgs a{};
-  a.x = x_routed;
+  a.x = x;
+  a.perm = perm;
+  a.T = T;
+  a.k = k;
   a.offsets = expert_offsets;
   a.values = w->values;
   a.masks = w->masks;
@@ -608,4 +628,30 @@ extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
   a.N = w->N;
   a.K = w->K;
   return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout == MOESQ_LAYOUT_TILED, stream);
+}
+
+extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
+                                               const int32_t *expert_offsets, int32_t M,
+                                               const moesq_weights_t *w, int32_t epilogue,
+                                               uint16_t *y, void *ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return spgemm_entry("moesq_grouped_spgemm", x_routed, nullptr, 0, 1, expert_offsets, M, w,
+                      epilogue, y, stream);
+}
+
+extern "C" moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const int32_t *perm,
+                                                      int32_t T, int32_t k,
+                                                      const int32_t *expert_offsets,
+                                                      const moesq_weights_t *w, int32_t epilogue,
+                                                      uint16_t *y, void *ws, size_t ws_bytes,
+                                                      hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffll)
+    return fail(MOESQ_ERR_SHAPE, "moesq_grouped_spgemm_gather: need T >= 0, k >= 1, T*k < 2^31");
+  if (T > 0 && !perm) return fail(MOESQ_ERR_NULL, "moesq_grouped_spgemm_gather: perm is NULL");
+  return spgemm_entry("moesq_grouped_spgemm_gather", x, perm, T, k, expert_offsets, T * k, w,
+                      epilogue, y, stream);
 }

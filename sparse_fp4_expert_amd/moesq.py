@@ -49,6 +49,8 @@ _permute = _sig("moesq_permute", _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _spgemm = _sig("moesq_grouped_spgemm", _i32, _vp, _vp, _i32, ctypes.POINTER(WeightsDesc), _i32,
                _vp, _vp, _sz, _vp)
 _spgemm_ws = _sig("moesq_spgemm_workspace_bytes", _sz, _i32, ctypes.POINTER(WeightsDesc))
+_spgemm_gather = _sig("moesq_grouped_spgemm_gather", _i32, _vp, _vp, _i32, _i32, _vp,
+                      ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _sz, _vp)
 _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
@@ -60,7 +62,8 @@ _last_error = _sig("moesq_last_error", ctypes.c_char_p)
 _version = _sig("moesq_version", _i32)
 
 EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
-            "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes", "moesq_unpermute",
+            "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes",
+            "moesq_grouped_spgemm_gather", "moesq_unpermute",
             "moesq_pack_weights", "moesq_tile_weights", "moesq_decode_weights",
             "moesq_validate", "moesq_status_string",
             "moesq_last_error", "moesq_version"]
@@ -171,6 +174,14 @@ def moesq_grouped_spgemm(x_routed, expert_offsets, M: int, w: Weights, epilogue:
                    _stream(stream)))
 
 
+def moesq_grouped_spgemm_gather(x, perm, T: int, k: int, expert_offsets, w: Weights,
+                                epilogue: int, y, ws=None, stream=None):
+    _check(_spgemm_gather(_ptr(x, torch.bfloat16, "x"), _ptr(perm, torch.int32, "perm"), T, k,
+                          _ptr(expert_offsets, torch.int32, "expert_offsets"), ctypes.byref(w.desc),
+                          epilogue, _ptr(y, torch.bfloat16, "y"), _ptr(ws, torch.uint8, "ws", True),
+                          0 if ws is None else ws.numel(), _stream(stream)))
+
+
 def moesq_spgemm_workspace_bytes(M: int, w: Weights) -> int:
     return int(_spgemm_ws(M, ctypes.byref(w.desc)))
 
@@ -245,6 +256,17 @@ def grouped_spgemm(x_routed, expert_offsets, w: Weights, epilogue: int = EPI_NON
     if out is None:
         out = torch.empty(M, n_out, dtype=torch.bfloat16, device=x_routed.device)
     moesq_grouped_spgemm(x_routed, expert_offsets, M, w, epilogue, out, None, stream)
+    return out
+
+
+def grouped_spgemm_gather(x, perm, k: int, expert_offsets, w: Weights, epilogue: int = EPI_NONE,
+                          out=None, stream=None):
+    """Dispatch fused into the GEMM: routed row r reads token perm[r] // k of x."""
+    T = x.shape[0]
+    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    if out is None:
+        out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=x.device)
+    moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets, w, epilogue, out, None, stream)
     return out
 
 

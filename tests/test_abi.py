@@ -115,3 +115,17 @@ def test_validate_rejects(m):
     assert v(None, 0, 1, 1, None, ref(_desc(m, layout=7)), None, None) == m.ERR_LAYOUT
     assert v(None, 0, 1, 1, None, ref(_desc(m, null=True)), None, None) == m.ERR_NULL
     assert v(None, 0, 1, 1, None, ref(_desc(m, K=48)), None, None) == m.ERR_SHAPE
+
+
+def test_spgemm_gather_rejects(m):
+    g = m._spgemm_gather
+    ref = ctypes.byref
+    d = ref(_desc(m))
+    assert g(0x10, 0x10, -1, 2, 0x10, d, 0, 0x10, None, 0, None) == m.ERR_SHAPE      # T < 0
+    assert g(0x10, 0x10, 4, 0, 0x10, d, 0, 0x10, None, 0, None) == m.ERR_SHAPE       # k < 1
+    assert g(0x10, 0x10, 1 << 30, 4, 0x10, d, 0, 0x10, None, 0, None) == m.ERR_SHAPE  # T*k >= 2^31
+    assert g(0x10, None, 4, 2, 0x10, d, 0, 0x10, None, 0, None) == m.ERR_NULL        # perm NULL
+    assert g(0x10, 0x10, 4, 2, None, d, 0, 0x10, None, 0, None) == m.ERR_NULL        # offsets NULL
+    assert g(0x10, 0x10, 4, 2, 0x10, ref(_desc(m, layout=7)), 0, 0x10, None, 0, None) == m.ERR_LAYOUT
+    assert g(0x10, 0x10, 4, 2, 0x10, d, 5, 0x10, None, 0, None) == m.ERR_ARG         # epilogue
+    assert g(None, None, 0, 2, 0x10, d, 0, None, None, 0, None) == m.OK              # T = 0

@@ -309,6 +309,30 @@ def test_spgemm_edges_tiled(lib, loads, N, K, swiglu):
     _edge_case(lib, loads, N, K, swiglu, seed=sum(loads) + N + K + 1, tiled=True)
 
 
+@pytest.mark.parametrize("name,swiglu", [("tiny", False), ("decode-30b", False),
+                                         ("prefill-30b", False), ("decode-1t", True)])
+def test_spgemm_gather_matches_permute(lib, name, swiglu):
+    """Dispatch fused into the GEMM gives the bytes of permute + GEMM, also
+    where the permutation has out-of-range entries (zero rows)."""
+    wl = synth.WORKLOADS[name]
+    ids, _ = synth.routing(wl)
+    w = lib.tile_weights(pack_workload(lib, wl, 0))
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    x = synth.tokens(wl).cuda()
+    epi = lib.EPI_SWIGLU if swiglu else lib.EPI_NONE
+    want = lib.grouped_spgemm(lib.permute(x, perm, wl.k), off, w, epi)
+    got = lib.grouped_spgemm_gather(x, perm, wl.k, off, w, epi)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    bad = perm.clone()
+    bad[[0, wl.M // 2, wl.M - 1]] = torch.tensor([-1, wl.M, 1 << 30], dtype=torch.int32, device=bad.device)
+    want = lib.grouped_spgemm(lib.permute(x, bad, wl.k), off, w, epi)
+    got = lib.grouped_spgemm_gather(x, bad, wl.k, off, w, epi)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert not got[[0, wl.M // 2, wl.M - 1]].any()
+
+
 @pytest.mark.parametrize("name", ["decode-30b", "prefill-30b"])
 def test_spgemm_30b_workloads(lib, name):
     """Full-size 30B-class workloads; sampled experts are checked against the
@@ -355,9 +379,8 @@ def test_chain_1t_workloads(lib, name):
     w2 = pack_workload(lib, wl, 1)
     w1t, w2t = lib.tile_weights(w1), lib.tile_weights(w2)
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
-    xr = lib.permute(x.cuda(), perm, wl.k)
-    say(f"[{name}] chain M={wl.M} (tiled weights)")
-    h = lib.grouped_spgemm(xr, off, w1t, lib.EPI_SWIGLU)
+    say(f"[{name}] chain M={wl.M} (tiled weights, dispatch fused into the gate/up GEMM)")
+    h = lib.grouped_spgemm_gather(x.cuda(), perm, wl.k, off, w1t, lib.EPI_SWIGLU)
     y2 = lib.grouped_spgemm(h, off, w2t)
     tw_d = torch.from_numpy(tw).cuda()
     out = lib.unpermute(y2, inv, tw_d if wl.weighted_combine else None, wl.T, wl.k)

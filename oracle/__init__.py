@@ -28,6 +28,8 @@ tiny inputs, invariances and hand-derived fixtures in tests/golden/.
 from .formats import (E2M1_VALUES, E4M3_VALUES, bf16_round, e2m1_decode,
                       e2m1_encode, e4m3_decode, e4m3_encode)
 from .pack import PackedExpert, decode, quantize, support
+from .paired import (PAIRS, PackedPairedExpert, decode_paired, paired_pattern,
+                     paired_support, pattern_mask, quantize_paired)
 from .route import route
 from .moe import (grouped_gemm, moe_chain, permute, silu, swiglu, unpermute,
                   expert_gemm)
@@ -46,4 +48,10 @@ READINGS = {
     "swiglu": "gate = first N/2 output columns, up = second N/2; "
               "h = silu(gate) * up, stored as bf16",
     "combine": "out[t] = sum_j w[t,j] * Y[row of (t,j)], j ascending",
+    "paired_index": "paired 4:8 pattern index p in [0,6) numbers the kept pair "
+                    "couples (0,1) (0,2) (0,3) (1,2) (1,3) (2,3); two per byte, "
+                    "even group in the low nibble",
+    "paired_support": "keep the two pairs with the largest fp32 |w_2i|+|w_2i+1|; "
+                      "equal sums -> lower pair index",
+    "paired_values": "kept values quantised exactly as the 4:8 format",
 }

@@ -57,20 +57,22 @@ def masks_of(keep: np.ndarray) -> np.ndarray:
     return bits.sum(axis=2).astype(np.uint8)
 
 
-def quantize(Wd: np.ndarray) -> PackedExpert:
-    """Compress a dense fp32 [N, K] expert matrix.
+def quantize_kept(Wd: np.ndarray, keep: np.ndarray):
+    """Codes of the kept weights of a dense fp32 [N, K] matrix under the
+    keep-map `keep` [N, K] (four kept positions per group of 8).
 
     All arithmetic that decides a code is done in fp32, in this order:
       g     = amax / 2688          (2688 = 6 * 448; g = 1 if amax == 0)
       six_g = 6 * g
       s     = E4M3(amax_32 / six_g)             per 32-position block
       q     = E2M1(w / (value(s) * g))          per kept weight
-    """
+    amax and amax_32 run over kept positions only.  Returns the kept codes
+    [N, K/8, 4] (ascending position per group), the scale codes [N, K/32]
+    and g."""
     Wd = np.ascontiguousarray(Wd, dtype=np.float32)
     N, K = Wd.shape
     if K % 32:
         raise ValueError("K must be a multiple of 32")
-    keep = support(Wd)
     a = np.abs(Wd)
     amax = np.float32(a[keep].max()) if a.size else np.float32(0)
     g = np.float32(amax / np.float32(2688.0)) if amax > 0 else np.float32(1.0)
@@ -84,30 +86,59 @@ def quantize(Wd: np.ndarray) -> PackedExpert:
         q = np.where(sg_full > 0, Wd / np.where(sg_full > 0, sg_full, 1), 0).astype(np.float32)
     codes = e2m1_encode(q)                                   # [N, K]
     kept = codes.reshape(N, K // 8, 8)[keep.reshape(N, K // 8, 8)].reshape(N, K // 8, 4)
-    kept = kept.astype(np.uint8)
-    values = np.empty((N, K // 8, 2), np.uint8)
+    return kept.astype(np.uint8), s_code, g
+
+
+def pack_nibbles(kept: np.ndarray) -> np.ndarray:
+    """[N, K/8, 4] kept codes -> [N, K/4] bytes: kept values 0,1 in the first
+    byte of the group, 2,3 in the second, the lower one in the low nibble."""
+    N, G, _ = kept.shape
+    values = np.empty((N, G, 2), np.uint8)
     values[:, :, 0] = kept[:, :, 0] | (kept[:, :, 1] << 4)
     values[:, :, 1] = kept[:, :, 2] | (kept[:, :, 3] << 4)
-    return PackedExpert(values.reshape(N, K // 4), masks_of(keep), s_code, g)
+    return values.reshape(N, 2 * G)
+
+
+def unpack_nibbles(values: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles: [N, K/4] bytes -> [N, K/8, 4] codes."""
+    N = values.shape[0]
+    v = values.reshape(N, -1, 2)
+    return np.stack([v[:, :, 0] & 15, v[:, :, 0] >> 4, v[:, :, 1] & 15, v[:, :, 1] >> 4], axis=2)
+
+
+def quantize(Wd: np.ndarray) -> PackedExpert:
+    """Compress a dense fp32 [N, K] expert matrix: the support of `support`,
+    then the codes of `quantize_kept`."""
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    N, K = Wd.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    keep = support(Wd)
+    kept, s_code, g = quantize_kept(Wd, keep)
+    return PackedExpert(pack_nibbles(kept), masks_of(keep), s_code, g)
+
+
+def decode_kept(codes4: np.ndarray, bits: np.ndarray, scales: np.ndarray, g,
+                include_global: bool = True) -> np.ndarray:
+    """Dense float64 [N, K] from the kept codes [N, K/8, 4] and the keep-map
+    [N, K/8, 8] (four set per group): w = E2M1(c_j) * E4M3(s_b) (* g) at the
+    j-th kept position of the group, 0 elsewhere.  Exact in float64."""
+    N, G, _ = bits.shape
+    K = 8 * G
+    rank = np.clip(np.cumsum(bits, axis=2) - 1, 0, 3)          # index j of each kept position
+    code = np.take_along_axis(codes4, rank, axis=2)
+    val = np.where(bits, E2M1_VALUES[code], 0.0).reshape(N, K)
+    w = val * np.repeat(E4M3_VALUES[scales], 32, axis=1)
+    if include_global:
+        w = w * np.float64(g)
+    return w
 
 
 def decode(p: PackedExpert, include_global: bool = True) -> np.ndarray:
     """Dense float64 [N, K] matrix the packed expert stands for:
     w[n, 8g+i] = E2M1(c_j) * E4M3(s_b) * g at the j-th set bit i of the mask,
     0 elsewhere.  Exact in float64."""
-    N = p.masks.shape[0]
-    K = p.masks.shape[1] * 8
     bits = ((p.masks[:, :, None].astype(np.uint32) >> np.arange(8)) & 1).astype(bool)
     if (bits.sum(axis=2) != 4).any():
         raise ValueError("every mask byte must have exactly four bits set")
-    v = p.values.reshape(N, K // 8, 2)
-    codes4 = np.stack([v[:, :, 0] & 15, v[:, :, 0] >> 4, v[:, :, 1] & 15, v[:, :, 1] >> 4],
-                      axis=2)                                  # [N, K/8, 4]
-    rank = np.clip(np.cumsum(bits, axis=2) - 1, 0, 3)          # index j of each set bit
-    code = np.take_along_axis(codes4, rank, axis=2)
-    val = np.where(bits, E2M1_VALUES[code], 0.0).reshape(N, K)
-    scale = np.repeat(E4M3_VALUES[p.scales], 32, axis=1)
-    w = val * scale
-    if include_global:
-        w = w * np.float64(p.g)
-    return w
+    return decode_kept(unpack_nibbles(p.values), bits, p.scales, p.g, include_global)

@@ -339,7 +339,112 @@ def pin_swiglu(O):
     assert np.allclose(h, [[0.0, 3.0 / (1.0 + math.exp(-1.0))]], rtol=1e-15)
 
 
+# ---------------------------------------------------------------- paired 4:8
+
+def pin_paired_fixture(O):
+    """The hand-derived paired 2 x 32 compression and the pattern table
+    (tests/golden/paired_rows.txt)."""
+    lines = _lines("paired_rows.txt")
+    d = {ln[0]: ln[1:] for ln in lines if ln[0] != "pattern"}
+    for ln in lines:
+        if ln[0] == "pattern":
+            p, pos = int(ln[1]), [int(v) for v in ln[2:]]
+            assert O.pattern_mask(p) == sum(1 << i for i in pos), (p, O.pattern_mask(p))
+    w0 = np.array([float(v) for v in d["w0"]], np.float32)
+    W = np.stack([w0, -w0])
+    p = O.quantize_paired(W)
+    assert float(p.g) == float(d["g"][0])
+    for r in range(2):
+        assert np.array_equal(p.values[r], _hex(d[f"values{r}"])), (r, p.values[r])
+        assert np.array_equal(p.patterns[r], _hex(d["patterns0"])), (r, p.patterns[r])
+        assert np.array_equal(p.scales[r], _hex(d["scales0"])), (r, p.scales[r])
+    want = np.float64([float(v) for v in d["decoded0"]])
+    dec = O.decode_paired(p)
+    assert np.array_equal(dec[0], want)
+    assert np.array_equal(dec[1], -want)
+    # decoding without the global scale divides by g exactly
+    assert np.array_equal(O.decode_paired(p, include_global=False)[0], want / float(p.g))
+
+
+def pin_paired_support_bruteforce(O, seed=10):
+    """Every group keeps the unique couple of pairs whose members both beat
+    both dropped pairs (larger fp32 |w| sum, or equal and lower index), found
+    by enumerating the six allowed patterns; that couple also has the largest
+    exact total, and the keep-map is its pattern's mask."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((6, 96)).astype(np.float32)
+    W[0, :8] = 1.0                                   # all four sums equal
+    W[1, 8:16] = [2, 0, 0, 2, 1, 1, -2, 0]           # sums 2 2 2 2
+    W[2, :8] = 0.0
+    W[3, 16:24] = [0, 0, 1, 0, 0, 1, 0.5, 0.5]       # sums 0 1 1 1
+    W[4, :] = np.round(W[4, :] * 2) / 2              # many equal sums
+    pat = O.paired_pattern(W)
+    keep = O.paired_support(W)
+    a = np.abs(W)
+    couples = [tuple(sorted(c)) for c in itertools.combinations(range(4), 2)]
+    assert sorted(O.PAIRS) == couples and len(set(O.PAIRS)) == 6
+    for n in range(W.shape[0]):
+        for g in range(W.shape[1] // 8):
+            grp = a[n, 8 * g:8 * g + 8]
+            sums = [np.float32(grp[2 * i] + grp[2 * i + 1]) for i in range(4)]
+            winners = [S for S in couples
+                       if all(sums[i] > sums[j] or (sums[i] == sums[j] and i < j)
+                              for i in S for j in range(4) if j not in S)]
+            assert len(winners) == 1
+            got = O.PAIRS[pat[n, g]]
+            assert got == winners[0], (n, g, got, winners)
+            best = max(Fraction(float(sums[i])) + Fraction(float(sums[j])) for i, j in couples)
+            assert Fraction(float(sums[got[0]])) + Fraction(float(sums[got[1]])) == best
+            kept = [i for i in range(8) if keep[n, 8 * g + i]]
+            assert kept == [2 * got[0], 2 * got[0] + 1, 2 * got[1], 2 * got[1] + 1]
+
+
+def pin_paired_layout(O, seed=11):
+    """Pattern masks are exactly the six unions of two adjacent pairs (the
+    golden set); a random matrix uses all six; packed size is the pages'
+    2.75 bits per logical weight plus the fp32 global scale."""
+    d = {ln[0]: ln[1:] for ln in _lines("layout.txt")}
+    pairs = [0x03, 0x0C, 0x30, 0xC0]
+    unions = {a | b for a, b in itertools.combinations(pairs, 2)}
+    masks = {O.pattern_mask(p) for p in range(6)}
+    assert masks == unions == {int(x, 16) for x in d["paired_patterns"]}
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    p = O.quantize_paired(W)
+    nib = np.stack([p.patterns & 15, p.patterns >> 4], -1)
+    assert set(np.unique(nib).tolist()) == set(range(6))
+    N, K = W.shape
+    assert p.nbytes * 8 == N * K * float(d["paired_bits_per_weight"][0]) + 32
+    assert p.values.shape == (N, K // 4) and p.patterns.shape == (N, K // 16)
+    assert p.scales.shape == (N, K // 32)
+
+
+def pin_paired_matches_48(O, seed=12):
+    """When the four largest |w| of every group form two adjacent pairs that
+    also have the two largest pair sums, the paired and the 4:8 formats keep
+    the same positions, so their decodes agree exactly; dropped positions
+    decode to zero."""
+    rng = np.random.default_rng(seed)
+    N, K = 16, 256
+    W = (rng.uniform(0, 0.1, (N, K)) * rng.choice([-1, 1], (N, K))).astype(np.float32)
+    for n in range(N):
+        for g in range(K // 8):
+            for i in rng.choice(4, 2, replace=False):
+                W[n, 8 * g + 2 * i:8 * g + 2 * i + 2] = rng.uniform(1, 2, 2) * rng.choice([-1, 1], 2)
+    big = np.flatnonzero(np.abs(W[3, 40:48]) >= 1) + 40
+    W[3, big] *= 20.0                                 # an outlier group
+    pp = O.quantize_paired(W)
+    p4 = O.quantize(W)
+    assert np.array_equal(O.paired_support(W), O.support(W))
+    d = O.decode_paired(pp)
+    assert np.array_equal(d, O.decode(p4))
+    assert (d[~O.paired_support(W)] == 0).all()
+    assert np.array_equal(pp.scales, p4.scales) and pp.g == p4.g
+
+
 ALL_PINS = [pin_e2m1_grid, pin_e4m3_table, pin_e4m3_encode, pin_e2m1_encode,
             pin_bf16_round, pin_quant_fixture, pin_support_bruteforce,
             pin_masks_and_layout, pin_quant_nearest, pin_route_bruteforce,
-            pin_gemm_exact, pin_gemm_invariances, pin_unpermute, pin_swiglu]
+            pin_gemm_exact, pin_gemm_invariances, pin_unpermute, pin_swiglu,
+            pin_paired_fixture, pin_paired_support_bruteforce, pin_paired_layout,
+            pin_paired_matches_48]

@@ -120,3 +120,56 @@ def test_swiglu_halves_swapped():
 
 def test_silu_sign():
     _fails(pins.pin_swiglu, _ns(silu=lambda x: np.asarray(x) / (1 + np.exp(np.asarray(x)))))
+
+
+# ---------------------------------------------------------------- paired 4:8
+
+import oracle.paired  # noqa: E402
+
+
+def test_paired_pattern_order(monkeypatch):
+    # (0,3) and (1,2) numbered the other way round
+    monkeypatch.setattr(oracle.paired, "PAIRS", ((0, 1), (0, 2), (1, 2), (0, 3), (1, 3), (2, 3)))
+    _fails(pins.pin_paired_fixture, oracle)
+
+
+def test_paired_pattern_nibbles_swapped():
+    real = oracle.quantize_paired
+
+    def q(W):
+        p = real(W)
+        p.patterns = ((p.patterns >> 4) | (p.patterns << 4)).astype(np.uint8)
+        return p
+    _fails(pins.pin_paired_fixture, _ns(quantize_paired=q))
+
+
+def test_paired_ties_to_higher_pair():
+    def pat(W):
+        N, K = W.shape
+        a = np.abs(np.asarray(W, np.float32)).reshape(N, K // 8, 4, 2)
+        s = (a[..., 0] + a[..., 1])[..., ::-1]
+        order = 3 - np.argsort(-s, axis=2, kind="stable")
+        i, j = np.minimum(order[..., 0], order[..., 1]), np.maximum(order[..., 0], order[..., 1])
+        lk = {c: n for n, c in enumerate(oracle.PAIRS)}
+        return np.vectorize(lambda x, y: lk[(x, y)])(i, j).astype(np.uint8)
+    _fails(pins.pin_paired_support_bruteforce, _ns(paired_pattern=pat))
+
+
+def test_paired_max_instead_of_sum():
+    def pat(W):
+        N, K = W.shape
+        a = np.abs(np.asarray(W, np.float32)).reshape(N, K // 8, 4, 2)
+        s = np.maximum(a[..., 0], a[..., 1])
+        order = np.argsort(-s, axis=2, kind="stable")
+        i, j = np.minimum(order[..., 0], order[..., 1]), np.maximum(order[..., 0], order[..., 1])
+        lk = {c: n for n, c in enumerate(oracle.PAIRS)}
+        return np.vectorize(lambda x, y: lk[(x, y)])(i, j).astype(np.uint8)
+    _fails(pins.pin_paired_support_bruteforce, _ns(paired_pattern=pat))
+
+
+def test_paired_decode_pair_offset(monkeypatch):
+    # pairs counted from the top of the group: pair i = positions 6-2i, 7-2i
+    monkeypatch.setattr(oracle.paired, "pattern_mask",
+                        lambda p: (3 << (6 - 2 * oracle.PAIRS[p][0])) | (3 << (6 - 2 * oracle.PAIRS[p][1])))
+    _fails(pins.pin_paired_matches_48, oracle)
+    _fails(pins.pin_paired_fixture, oracle)

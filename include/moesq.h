@@ -66,6 +66,8 @@ typedef enum {
 
 #define MOESQ_LAYOUT_CANONICAL 0
 #define MOESQ_LAYOUT_TILED 1
+#define MOESQ_LAYOUT_PAIRED 2
+#define MOESQ_LAYOUT_PAIRED_TILED 3
 
 /* Limits of this build. */
 #define MOESQ_MAX_EXPERTS 1024
@@ -98,7 +100,7 @@ typedef struct {
   const uint8_t *scales;
   const float *global_scale;
   int32_t E, N, K;
-  int32_t layout; /* MOESQ_LAYOUT_CANONICAL or MOESQ_LAYOUT_TILED */
+  int32_t layout; /* MOESQ_LAYOUT_CANONICAL, _TILED, _PAIRED or _PAIRED_TILED */
 } moesq_weights_t;
 
 /*
@@ -113,6 +115,39 @@ typedef struct {
  *
  * Inside a segment the byte order is the canonical one.  Sizes per array
  * equal the canonical sizes.
+ */
+
+/*
+ * MOESQ_LAYOUT_PAIRED: the pages' paired 4:8 format ("A Sparse-quantized
+ * representation": each group of eight keeps two of its four adjacent pairs,
+ * six patterns; "Storage layout": four kept values and a pattern index per
+ * group plus a UE4M3 scale per 32 weights, 2.75 bits per weight).  The
+ * `masks` pointer carries the pattern indices:
+ *
+ *   values [E][N][K/4]   as the canonical layout (four kept codes per group,
+ *                        ascending position, lower one in the low nibble)
+ *   masks  [E][N][K/16]  pattern index p of group g in byte g/2, the even
+ *                        group in the low nibble.  p in [0, 6) numbers the
+ *                        kept pair couples (0,1) (0,2) (0,3) (1,2) (1,3) (2,3),
+ *                        pair i being positions 2i and 2i+1 (caller contract:
+ *                        p < 6).
+ *   scales, global_scale as the canonical layout.
+ *
+ * MOESQ_LAYOUT_PAIRED_TILED: the GEMM's layout of paired weights (N % 32 == 0,
+ * K % 64 == 0), produced by moesq_tile_weights.  Segments as in
+ * MOESQ_LAYOUT_TILED; a "unit" u (0..3) of a row's segment is its groups
+ * G = 2u and G' = 2u+1, read as the windows [G even positions, G' even,
+ * G odd, G' odd] (positions 0,2,4,6 / 1,3,5,7 of a group):
+ *
+ *   values [E][N/32][K/64][32][16]  dword u: eight E2M1 codes in nibbles 0..7
+ *                                   = G v0, G v2, G' v0, G' v2, G v1, G v3,
+ *                                   G' v1, G' v3 (v0..v3: the group's kept
+ *                                   codes in ascending position)
+ *   masks  [E][N/32][K/64][32][4]   byte u: w(G) | w(G') << 4, where
+ *                                   w = i | j << 2 for kept pairs i < j
+ *   scales [E][N/32][K/64][32][2]   as MOESQ_LAYOUT_TILED
+ *
+ * Array sizes equal those of MOESQ_LAYOUT_PAIRED.
  */
 
 /*
@@ -153,7 +188,10 @@ moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, 
  *                      c < N/2, y is [M][N/2]  (gate = first half of W rows)
  *   x_routed        [M][K] bf16, expert-sorted rows (moesq_permute output)
  *   expert_offsets  [E+1] int32 (moesq_route output); offsets are clamped to [0, M]
- *   w               host pointer to the weight descriptor
+ *   w               host pointer to the weight descriptor: layout CANONICAL,
+ *                   TILED or PAIRED_TILED (paired weights run on the sparse
+ *                   MFMA; the canonical paired layout is an exchange format
+ *                   and returns MOESQ_ERR_LAYOUT: tile it first)
  *   ws, ws_bytes    workspace; moesq_spgemm_workspace_bytes() bytes (may be 0)
  * Rows of y outside every expert range are not written.
  * Limits: K % 32 == 0, N % 16 == 0 (SWIGLU: N % 32 == 0), E <= MOESQ_MAX_EXPERTS,
@@ -213,9 +251,28 @@ moesq_status_t moesq_pack_weights(const float *dense, int32_t E, int32_t N, int3
                                   float *global_scale, hipStream_t stream);
 
 /*
- * Re-lay canonical weights into MOESQ_LAYOUT_TILED (a pure byte permutation).
- *   src: canonical descriptor (host struct, device buffers).  values, masks,
- *   scales: device outputs of the canonical sizes; they must not alias src.
+ * Compress dense fp32 experts into MOESQ_LAYOUT_PAIRED ("A Sparse-quantized
+ * representation", Blackwell paired 4:8 NVFP4 and Storage layout).  As
+ * moesq_pack_weights, except the support: in every group of 8 the two pairs
+ * (2i, 2i+1) with the largest |w_2i| + |w_2i+1| (fp32 sum) are kept, equal
+ * sums to the lower pair; amax and the block maxima run over kept weights.
+ *   dense [E][N][K] fp32 in; values [E][N][K/4], patterns [E][N][K/16],
+ *   scales [E][N][K/32], global_scale [E] out.
+ * Limits: K % 32 == 0, N >= 1, 1 <= E <= 65535.
+ */
+moesq_status_t moesq_pack_weights_paired(const float *dense, int32_t E, int32_t N, int32_t K,
+                                         uint8_t *values, uint8_t *patterns, uint8_t *scales,
+                                         float *global_scale, hipStream_t stream);
+
+/*
+ * Re-lay canonical weights into MOESQ_LAYOUT_TILED (a pure byte permutation),
+ * or MOESQ_LAYOUT_PAIRED weights into MOESQ_LAYOUT_PAIRED_TILED (codes
+ * reordered into the window order, pattern indices re-encoded as window
+ * positions; an index above 5 becomes positions (0, 0), of unspecified
+ * effect).
+ *   src: CANONICAL or PAIRED descriptor (host struct, device buffers).
+ *   values, masks, scales: device outputs of the source sizes; they must not
+ *   alias src.
  *   The global scales are not touched (share src->global_scale).
  * Limits: N % 32 == 0, K % 64 == 0.
  */
@@ -223,7 +280,7 @@ moesq_status_t moesq_tile_weights(const moesq_weights_t *src, uint8_t *values, u
                                   uint8_t *scales, hipStream_t stream);
 
 /*
- * Decode one expert to dense bf16 WITHOUT the global scale (either layout):
+ * Decode one expert to dense bf16 WITHOUT the global scale (any layout):
  *   dense[n][k] = E2M1(code) * E4M3(scale) (exact in bf16) or 0.
  * Uses the same in-register decoder as moesq_grouped_spgemm; meant for
  * checking and debugging.  dense is [N][K] bf16.  0 <= expert < E.
@@ -240,7 +297,9 @@ moesq_status_t moesq_decode_weights(const moesq_weights_t *w, int32_t expert, ui
  * (w too) to skip its checks.
  *   topk_ids [T*k]     every id in [0, E)
  *   expert_offsets [E+1] offsets[0] == 0, non-decreasing, offsets[E] == T*k
- *   w (host struct)    every mask byte has exactly four bits set; every
+ *   w (host struct)    every mask byte has exactly four bits set (paired
+ *                      layouts: every pattern nibble is an index in [0, 6),
+ *                      or in the tiled layout valid window positions); every
  *                      scale byte is a non-negative finite E4M3 code (not
  *                      0x7F, sign bit clear); every global scale is finite
  *                      and >= 0.  Either layout (the checks are per byte).

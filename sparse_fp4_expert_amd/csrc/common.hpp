@@ -25,6 +25,7 @@ void clear_error();
 // ------------------------------------------------------------------ device side
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -102,6 +103,39 @@ __device__ __forceinline__ uint4 decode_group(uint32_t mask8, uint32_t vw, float
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ---- paired 4:8 ("Blackwell paired 4:8 NVFP4": two of the four adjacent
+// pairs of a group of eight are kept, six patterns).
+//
+// Reordering a group's positions as (0,2,4,6 | 1,3,5,7) turns every paired
+// pattern into 2:4 on both halves with the same two indices: kept pairs
+// i < j put one value at slots i and j of the even half and one at slots i
+// and j of the odd half.  The sparse MFMA of gfx950 takes exactly that: per
+// window of four dense K positions two compressed values and two 2-bit
+// positions.  A "unit" is two neighbouring groups G, G' (16 positions) read
+// as the four windows [G even, G' even, G odd, G' odd].
+
+// 2-bit window positions i | j << 2 of canonical pattern index p (pairs in
+// lexicographic order (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)); 0 for p > 5.
+__host__ __device__ inline uint32_t paired_window_index(uint32_t p) {
+  constexpr uint32_t t = 4u | 8u << 4 | 12u << 8 | 9u << 12 | 13u << 16 | 14u << 20;
+  return p < 6 ? (t >> (4 * p)) & 15u : 0u;
+}
+
+// Decodes a unit's eight compressed E2M1 codes (nibble i = compressed slot
+// i) times the block scale to bf16, slot order (slot 0 in the low half of
+// dword 0); exact, as in decode_group.
+__device__ __forceinline__ uint4 decode_paired_unit(uint32_t v, float scale) {
+  const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+  const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+  const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+  const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+  auto hi2 = [&](float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi * scale), __float_as_uint(lo * scale),
+                                 0x07060302u);
+  };
+  return make_uint4(hi2(a[0], a[1]), hi2(b[0], b[1]), hi2(c[0], c[1]), hi2(d[0], d[1]));
 }
 
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }

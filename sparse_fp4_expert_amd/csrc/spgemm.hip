@@ -222,12 +222,128 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, bool TILED>
+// ---- paired 4:8 weights on the sparse MFMA (v_smfmac_f32_16x16x64_bf16,
+// v_smfmac_f32_32x32x32_bf16).  Lane l holds A row l % MS and eight
+// compressed bf16 for the dense K range [16q, 16q+16), q = l / MS: one unit
+// (two groups as the windows [G even, G' even, G odd, G' odd]) with its
+// 2-bit window positions in the index operand.  B lane l holds token
+// l % MS: elements 0..7 are dense K 8q..8q+7 and elements 8..15 dense K
+// 8q+32..8q+39 (16x16x64) or 8q+16..8q+23 (32x32x32), i.e. the even or odd
+// half of a unit of lane group q >> 1 and of lane group (q >> 1) + LG/2.
+// The accumulator layout is that of the dense MFMA of the same shape.
+template <int MS>
+struct Smfmac;
+template <>
+struct Smfmac<16> {
+  using C = f32x4_t;
+  static __device__ __forceinline__ C run(uint4 a, bf16x16_t b, C c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), b, c, idx, 0, 0);
+  }
+};
+template <>
+struct Smfmac<32> {
+  using C = f32x16_t;
+  static __device__ __forceinline__ C run(uint4 a, bf16x16_t b, C c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a), b, c, idx, 0, 0);
+  }
+};
+
+// Paired tiled weights of one lane for one K chunk: per fragment, its lane
+// group's 64-position segment -- four units of eight codes, four window
+// bytes, two scale bytes.
+template <int RF>
+struct PChunk {
+  uint32_t v[RF][4];
+  uint32_t w[RF];
+  uint32_t s[RF];
+};
+
+template <int RF>
+__device__ __forceinline__ void load_pchunk(PChunk<RF> &c, __amdgpu_buffer_rsrc_t vr,
+                                            __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                            const uint32_t (&fv)[RF], const uint32_t (&fw)[RF],
+                                            const uint32_t (&fs)[RF], uint32_t lo) {
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vr, lo, fv[f], 0);
+    c.v[f][0] = v[0];
+    c.v[f][1] = v[1];
+    c.v[f][2] = v[2];
+    c.v[f][3] = v[3];
+    c.w[f] = __builtin_amdgcn_raw_buffer_load_b32(wr, lo >> 2, fw[f], 0);
+    c.s[f] = __builtin_amdgcn_raw_buffer_load_b16(sr, lo >> 3, fs[f], 0);
+  }
+}
+
+// Sparse MFMAs over one chunk staged in `tk`: a token row of the chunk holds
+// KC/16 units of 32 bytes, [8 even-position bf16 | 8 odd-position bf16],
+// whose 16-byte halves h sit at slot (2u + h) ^ (row % (KC/8)).  Step s
+// takes unit s of every lane group's segment; the A operands of step s+1
+// are decoded while the sparse MFMAs of step s run.
+template <int MS, int RF, int TF, int KC, bool FULL>
+__device__ __forceinline__ void mma_chunk_paired(typename Smfmac<MS>::C (&acc)[RF][TF],
+                                                 const uint16_t *tk, const PChunk<RF> &w, int nft,
+                                                 int q, int rl) {
+  constexpr int LG = 64 / MS;
+  constexpr int SLOTS = KC / 8;
+  float sf[RF][2];
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.s[f], 1.0f, false);
+    sf[f][0] = p[0];
+    sf[f][1] = p[1];
+  }
+  const int half = q & 1, ulo = 4 * (q >> 1), uhi = 4 * ((q >> 1) + LG / 2);
+  uint4 A[2][RF];
+  int I[2][RF];
+  auto dec = [&](uint4 (&a)[RF], int (&ix)[RF], int s) {
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+      a[f] = decode_paired_unit(w.v[f][s], sf[f][s >> 1]);
+      // window byte s into bytes 0 and 1: the same positions for both halves
+      ix[f] = (int)__builtin_amdgcn_perm(w.w[f], w.w[f], 0x0c0c0000u | (uint32_t)(s << 8) | (uint32_t)s);
+    }
+  };
+  auto load_b = [&](int t, int s) {
+    const int row = t * MS + rl;
+    const uint16_t *br = tk + row * KC;
+    const int sw = row & (SLOTS - 1);
+    const uint4 lo = *reinterpret_cast<const uint4 *>(br + 8 * ((2 * (ulo + s) + half) ^ sw));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(br + 8 * ((2 * (uhi + s) + half) ^ sw));
+    struct { uint4 l, h; } lh = {lo, hi};
+    return __builtin_bit_cast(bf16x16_t, lh);
+  };
+  dec(A[0], I[0], 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    // token fragments one ahead: two B operands (16 VGPRs) live, not TF
+    bf16x16_t B = load_b(0, s);
+    if (s + 1 < 4) dec(A[(s + 1) & 1], I[(s + 1) & 1], s + 1);
+#pragma unroll
+    for (int t = 0; t < TF; ++t) {
+      if (!FULL && t >= nft) break;
+      bf16x16_t Bn = B;
+      if (t + 1 < TF && (FULL || t + 1 < nft)) Bn = load_b(t + 1, s);
+#pragma unroll
+      for (int f = 0; f < RF; ++f)
+        acc[f][t] = Smfmac<MS>::run(A[s & 1][f], B, acc[f][t], I[s & 1][f]);
+      B = Bn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Weight formats of the kernel.
+enum { FMT_CANONICAL = 0, FMT_TILED = 1, FMT_PAIRED = 2 };
+
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(WAVES * 64)
 // 16-row tiles stream weights: at most 128 VGPRs, so that two 8-wave
 // workgroups share a CU.  32-row tiles hold 128 accumulators per lane.
 __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void spgemm_kernel(
     SpgemmArgs a) {
+  constexpr bool TILED = FMT != FMT_CANONICAL;
+  constexpr bool PAIRED = FMT == FMT_PAIRED;
   using MF = Mfma<MS>;
   constexpr int LG = 64 / MS;          // lane groups
   constexpr int BM = TF * MS;          // tokens per tile
@@ -253,7 +369,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.E, N = a.N, K = a.K, M = a.M;
 
-  build_group_lut(lut);
+  if constexpr (!PAIRED) build_group_lut(lut);
   for (int e = tid; e <= E; e += WAVES * 64) s_lo[e] = min(max(a.offsets[e], 0), M);
   __syncthreads();
   if (wave == 0) {
@@ -332,11 +448,13 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       }
     }
     const size_t erow = (size_t)e * N;
-    const uint8_t *vb = a.values + erow * vrow, *mb = a.masks + erow * mrow,
+    const uint8_t *vb = a.values + erow * vrow, *mb = a.masks + erow * (PAIRED ? mrow / 2 : mrow),
                   *sb = a.scales + erow * srow;
     const uint32_t ebytes = (uint32_t)(vrow * (size_t)N);   // value bytes of one expert
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, (int)ebytes, 0x20000);
-    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc((void *)mb, 0, (int)(ebytes >> 1), 0x20000);
+    // mask bytes: half the value bytes; paired window bytes: a quarter
+    const __amdgpu_buffer_rsrc_t mr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)mb, 0, (int)(ebytes >> (PAIRED ? 2 : 1)), 0x20000);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc((void *)sb, 0, (int)(ebytes >> 3), 0x20000);
     uint32_t fv[RF], fm[RF], fs[RF];
 #pragma unroll
@@ -345,7 +463,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       if constexpr (TILED) {
         const uint32_t blk = (r >> 5) * segs, rin = r & 31u;
         fv[f] = blk * 512u + rin * 16u;
-        fm[f] = blk * 256u + rin * 8u;
+        fm[f] = PAIRED ? blk * 128u + rin * 4u : blk * 256u + rin * 8u;
         fs[f] = blk * 64u + rin * 2u;
       } else {
         fv[f] = r * (uint32_t)vrow;
@@ -401,6 +519,35 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
             (__attribute__((address_space(3))) void *)(buf + (wave * BPW + j) * 512), 16, 0, 0);
       }
     };
+    // Paired weights: the sparse MFMA contracts each 16-position unit in the
+    // order [even positions | odd positions].  The direct-to-LDS loads above
+    // move whole dwords (position pairs), so once this wave's loads have
+    // landed (vmcnt(0): the count is per wave) every lane rewrites its own
+    // 16-byte slot in place: the slot pair (P, P^1) of a unit holds its two
+    // groups G, G' and becomes its even half and its odd half.  Lane L's
+    // slot P = L % UPR holds logical unit-half h = (P ^ row) & 1, the same
+    // for every 1 KB block of the lane, since a block starts at an even row
+    // and covers 64 / UPR rows.  Both slots are read before either is
+    // written: LDS instructions of one wave run in order.
+    const int split_h = ((lane % UPR) ^ (lane / UPR)) & 1;
+    const uint32_t split_sel = split_h ? 0x07060302u : 0x05040100u;
+    auto split_tok = [&](uint16_t *buf) {
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        if ((wave * BPW + j) * (64 / UPR) >= nrows) break;   // block never loaded
+        uint16_t *blk = buf + (wave * BPW + j) * 512;
+        const uint4 x = *reinterpret_cast<const uint4 *>(blk + 8 * lane);
+        const uint4 y = *reinterpret_cast<const uint4 *>(blk + 8 * (lane ^ 1));
+        // own group: dwords p0 p1; the neighbour's: p2 p3; G goes first
+        uint2 own, nbr;
+        own.x = __builtin_amdgcn_perm(x.y, x.x, split_sel);
+        own.y = __builtin_amdgcn_perm(x.w, x.z, split_sel);
+        nbr.x = __builtin_amdgcn_perm(y.y, y.x, split_sel);
+        nbr.y = __builtin_amdgcn_perm(y.w, y.z, split_sel);
+        *reinterpret_cast<uint2 *>(blk + 8 * lane + 4 * split_h) = own;
+        *reinterpret_cast<uint2 *>(blk + 8 * lane + 4 * (split_h ^ 1)) = nbr;
+      }
+    };
     // tiled: this lane's segment of the chunk at k0, clamped into K
     auto tlo = [&](int k0) {
       const uint32_t seg = min((uint32_t)(k0 >> 6) + (uint32_t)q, segs - 1u);
@@ -436,37 +583,70 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           load_wchunk(w, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
         }
       };
-      WChunk<RF, KQ> wA, wB;
-      load_w(wA, 0);
-      load_tok(tkA, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      // One chunk: prefetch chunk c + 1 into (nxt, wn), compute chunk c from
-      // (cur, wc).  The two token buffers are distinct LDS objects, so the
-      // reads of `cur` need not wait for the direct-to-LDS loads into `nxt`.
-      auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, WChunk<RF, KQ> &wc,
-                       WChunk<RF, KQ> &wn) {
-        if (c + 1 < nk) {
-          load_w(wn, (c + 1) * KC);
-          load_tok(nxt, (c + 1) * KC);
-        }
-        if constexpr (TILED) {
+      if constexpr (PAIRED) {
+        PChunk<RF> wA, wB;
+        load_pchunk(wA, vr, mr, sr, fv, fm, fs, tlo(0));
+        load_tok(tkA, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        split_tok(tkA);
+        __syncthreads();
+        auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, PChunk<RF> &wc,
+                         PChunk<RF> &wn) {
+          if (c + 1 < nk) {
+            load_pchunk(wn, vr, mr, sr, fv, fm, fs, tlo((c + 1) * KC));
+            load_tok(nxt, (c + 1) * KC);
+          }
           if ((c + 1) * KC > K) {
-            // segments past K were clamped to the last one: clear their masks
+            // segments past K were clamped to the last one: zero their codes
             const bool ok = (uint32_t)((c * KC) >> 6) + (uint32_t)q < segs;
 #pragma unroll
             for (int f = 0; f < RF; ++f)
 #pragma unroll
-              for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) wc.m[f][i] = ok ? wc.m[f][i] : 0u;
+              for (int i = 0; i < 4; ++i) wc.v[f][i] = ok ? wc.v[f][i] : 0u;
           }
+          mma_chunk_paired<MS, RF, TF, KC, FULL>(acc, cur, wc, nft, q, rl);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (c + 1 < nk) split_tok(nxt);
+          __syncthreads();
+        };
+        for (int c = 0; c < nk; c += 2) {
+          chunk(c, tkA, tkB, wA, wB);
+          if (c + 1 < nk) chunk(c + 1, tkB, tkA, wB, wA);
         }
-        mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
+      } else {
+        WChunk<RF, KQ> wA, wB;
+        load_w(wA, 0);
+        load_tok(tkA, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-      };
-      for (int c = 0; c < nk; c += 2) {
-        chunk(c, tkA, tkB, wA, wB);
-        if (c + 1 < nk) chunk(c + 1, tkB, tkA, wB, wA);
+        // One chunk: prefetch chunk c + 1 into (nxt, wn), compute chunk c from
+        // (cur, wc).  The two token buffers are distinct LDS objects, so the
+        // reads of `cur` need not wait for the direct-to-LDS loads into `nxt`.
+        auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, WChunk<RF, KQ> &wc,
+                         WChunk<RF, KQ> &wn) {
+          if (c + 1 < nk) {
+            load_w(wn, (c + 1) * KC);
+            load_tok(nxt, (c + 1) * KC);
+          }
+          if constexpr (TILED) {
+            if ((c + 1) * KC > K) {
+              // segments past K were clamped to the last one: clear their masks
+              const bool ok = (uint32_t)((c * KC) >> 6) + (uint32_t)q < segs;
+  #pragma unroll
+              for (int f = 0; f < RF; ++f)
+  #pragma unroll
+                for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) wc.m[f][i] = ok ? wc.m[f][i] : 0u;
+            }
+          }
+          mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+        };
+        for (int c = 0; c < nk; c += 2) {
+          chunk(c, tkA, tkB, wA, wB);
+          if (c + 1 < nk) chunk(c + 1, tkB, tkA, wB, wA);
+        }
+
       }
 
       // Epilogue.  Accumulator element r of a lane holds weight row
@@ -520,10 +700,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, bool TILED>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT>
 static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
-  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, TILED>;
+  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   // upper bound of the item count: every expert may hold one partial tile
   const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
@@ -555,27 +735,38 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // feeds 4 MFMAs of 32 tokens.  Fragments are whole: the 32-row tile needs
 // the output rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the
 // 16-row tile runs.
-template <bool TILED>
+// Paired weights take the same two tiles on the sparse MFMA
+// (16x16x64 and 32x32x32): the same token and weight-row counts per wave,
+// each step contracting twice the dense K.
+template <int FMT>
 static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
   const bool small = (long long)a.M <= 32ll * a.E || out_rows % 32 != 0;
   if (small)
-    return swiglu ? launch_one<8, 16, 2, 2, 256, true, TILED>(a, stream)
-                  : launch_one<8, 16, 2, 2, 256, false, TILED>(a, stream);
-  return swiglu ? launch_one<8, 32, 2, 4, 128, true, TILED>(a, stream)
-                : launch_one<8, 32, 2, 4, 128, false, TILED>(a, stream);
+    return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
+                  : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
+                : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
 }
 
-static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, bool tiled,
+static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, int layout,
                                     hipStream_t stream) {
-  return tiled ? launch_layout<true>(a, swiglu, stream) : launch_layout<false>(a, swiglu, stream);
+  switch (layout) {
+    case MOESQ_LAYOUT_TILED: return launch_layout<FMT_TILED>(a, swiglu, stream);
+    case MOESQ_LAYOUT_PAIRED_TILED: return launch_layout<FMT_PAIRED>(a, swiglu, stream);
+    default: return launch_layout<FMT_CANONICAL>(a, swiglu, stream);
+  }
 }
 
 static moesq_status_t check_weights(const moesq_weights_t *w, const char *who) {
   if (!w) return fail(MOESQ_ERR_NULL, std::string(who) + ": weight descriptor is NULL");
-  if (w->layout != MOESQ_LAYOUT_CANONICAL && w->layout != MOESQ_LAYOUT_TILED)
+  if (w->layout == MOESQ_LAYOUT_PAIRED)
+    return fail(MOESQ_ERR_LAYOUT, std::string(who) +
+                                      ": paired weights must be tiled first (moesq_tile_weights)");
+  if (w->layout != MOESQ_LAYOUT_CANONICAL && w->layout != MOESQ_LAYOUT_TILED &&
+      w->layout != MOESQ_LAYOUT_PAIRED_TILED)
     return fail(MOESQ_ERR_LAYOUT, std::string(who) + ": unknown weight layout");
-  if (w->layout == MOESQ_LAYOUT_TILED && (w->N % 32 || w->K % 64))
+  if (w->layout != MOESQ_LAYOUT_CANONICAL && (w->N % 32 || w->K % 64))
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": tiled layout needs N % 32 == 0, K % 64 == 0");
   if (!w->values || !w->masks || !w->scales || !w->global_scale)
     return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL weight buffer");
@@ -627,7 +818,7 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   a.E = w->E;
   a.N = w->N;
   a.K = w->K;
-  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout == MOESQ_LAYOUT_TILED, stream);
+  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout, stream);
 }
 
 extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,

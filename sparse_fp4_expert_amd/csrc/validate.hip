@@ -1,8 +1,9 @@
 // Debug check of the caller contracts the hot-path kernels rely on without
 // checking them: routed ids in range, consistent expert offsets, exactly four
 // kept positions per 4:8 group (the format keeps four values of every eight,
-// paper summary page, "A Sparse-quantized representation"), and block scales
-// that are non-negative finite E4M3 codes.  Each check counts its violations
+// paper summary page, "A Sparse-quantized representation"; for the paired
+// layouts, one of the six pair patterns per group), and block scales that
+// are non-negative finite E4M3 codes.  Each check counts its violations
 // in a small device array; the call synchronises and reports the counts.
 #include <string>
 
@@ -61,6 +62,17 @@ __global__ void check_bytes_kernel(const uint8_t *p, long long n, Pred pred, uns
 struct MaskNotFour {
   __device__ bool operator()(uint32_t m) const { return __builtin_popcount(m) != 4; }
 };
+// canonical paired: both pattern indices of the byte in [0, 6)
+struct PatternBad {
+  __device__ bool operator()(uint32_t b) const { return (b & 15u) > 5u || (b >> 4) > 5u; }
+};
+// paired tiled: both nibbles are window positions i | j << 2 with i < j,
+// i.e. one of 4, 8, 9, 12, 13, 14 (bits of 0x7310)
+struct WindowBad {
+  __device__ bool operator()(uint32_t b) const {
+    return !((0x7310u >> (b & 15u)) & 1u) || !((0x7310u >> (b >> 4)) & 1u);
+  }
+};
 // sign bit set, or the NaN code 0x7F
 struct ScaleBad {
   __device__ bool operator()(uint32_t s) const { return (s & 0x80u) || s == 0x7fu; }
@@ -96,7 +108,7 @@ extern "C" moesq_status_t moesq_validate(const int32_t *topk_ids, int32_t T, int
     if (T < 0 || k < 1) return fail(MOESQ_ERR_SHAPE, "moesq_validate: need T >= 0 and k >= 1");
   }
   if (w) {
-    if (w->layout != MOESQ_LAYOUT_CANONICAL && w->layout != MOESQ_LAYOUT_TILED)
+    if (w->layout < MOESQ_LAYOUT_CANONICAL || w->layout > MOESQ_LAYOUT_PAIRED_TILED)
       return fail(MOESQ_ERR_LAYOUT, "moesq_validate: unknown weight layout");
     if (w->E < 1 || w->N < 1 || w->K < 32 || w->K % 32)
       return fail(MOESQ_ERR_SHAPE, "moesq_validate: bad weight shape");
@@ -119,8 +131,15 @@ extern "C" moesq_status_t moesq_validate(const int32_t *topk_ids, int32_t T, int
   if (e == hipSuccess && w) {
     const long long groups = (long long)w->E * w->N * (w->K / 8);
     const long long blocks = (long long)w->E * w->N * (w->K / 32);
-    hipLaunchKernelGGL((check_bytes_kernel<V_MASKS, MaskNotFour>), dim3(grid_for(groups / 16 + 1, 256)),
-                       dim3(256), 0, stream, w->masks, groups, MaskNotFour{}, cnt);
+    if (w->layout == MOESQ_LAYOUT_PAIRED)
+      hipLaunchKernelGGL((check_bytes_kernel<V_MASKS, PatternBad>), dim3(grid_for(groups / 32 + 1, 256)),
+                         dim3(256), 0, stream, w->masks, groups / 2, PatternBad{}, cnt);
+    else if (w->layout == MOESQ_LAYOUT_PAIRED_TILED)
+      hipLaunchKernelGGL((check_bytes_kernel<V_MASKS, WindowBad>), dim3(grid_for(groups / 32 + 1, 256)),
+                         dim3(256), 0, stream, w->masks, groups / 2, WindowBad{}, cnt);
+    else
+      hipLaunchKernelGGL((check_bytes_kernel<V_MASKS, MaskNotFour>), dim3(grid_for(groups / 16 + 1, 256)),
+                         dim3(256), 0, stream, w->masks, groups, MaskNotFour{}, cnt);
     hipLaunchKernelGGL((check_bytes_kernel<V_SCALES, ScaleBad>), dim3(grid_for(blocks / 16 + 1, 256)),
                        dim3(256), 0, stream, w->scales, blocks, ScaleBad{}, cnt);
     hipLaunchKernelGGL(check_gscale_kernel, dim3(grid_for(w->E, 256)), dim3(256), 0, stream,
@@ -134,7 +153,7 @@ extern "C" moesq_status_t moesq_validate(const int32_t *topk_ids, int32_t T, int
   if (counts)
     for (int i = 0; i < V_COUNT; ++i) counts[i] = host[i];
   static const char *names[V_COUNT] = {"ids outside [0, E)", "offset violations",
-                                       "masks without exactly four bits",
+                                       "masks or pattern bytes outside the format",
                                        "scale bytes negative or NaN", "non-finite global scales"};
   std::string msg;
   for (int i = 0; i < V_COUNT; ++i)

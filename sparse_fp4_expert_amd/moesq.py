@@ -24,7 +24,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_LAYOUT, ERR_HIP, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
 EPI_NONE, EPI_SWIGLU = 0, 1
-LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+LAYOUT_CANONICAL, LAYOUT_TILED, LAYOUT_PAIRED, LAYOUT_PAIRED_TILED = 0, 1, 2, 3
+PAIRED_LAYOUTS = (LAYOUT_PAIRED, LAYOUT_PAIRED_TILED)
 MAX_EXPERTS = 1024
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -53,6 +54,8 @@ _spgemm_gather = _sig("moesq_grouped_spgemm_gather", _i32, _vp, _vp, _i32, _i32,
                       ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _sz, _vp)
 _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
+_pack_paired = _sig("moesq_pack_weights_paired", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                    _vp)
 _decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
 _tile = _sig("moesq_tile_weights", _i32, ctypes.POINTER(WeightsDesc), _vp, _vp, _vp, _vp)
 _validate = _sig("moesq_validate", _i32, _vp, _i32, _i32, _i32, _vp, ctypes.POINTER(WeightsDesc),
@@ -64,7 +67,8 @@ _version = _sig("moesq_version", _i32)
 EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes",
             "moesq_grouped_spgemm_gather", "moesq_unpermute",
-            "moesq_pack_weights", "moesq_tile_weights", "moesq_decode_weights",
+            "moesq_pack_weights", "moesq_pack_weights_paired", "moesq_tile_weights",
+            "moesq_decode_weights",
             "moesq_validate", "moesq_status_string",
             "moesq_last_error", "moesq_version"]
 
@@ -111,14 +115,17 @@ def _stream(stream):
 class Weights:
     """Device tensors of compressed experts.
 
-    values uint8 [E, N, K/4], masks uint8 [E, N, K/8], scales uint8 [E, N, K/32],
-    global_scale float32 [E].  `layout` is LAYOUT_CANONICAL or LAYOUT_TILED (the
-    same shapes; tiled bytes are permuted as include/moesq.h describes)."""
+    values uint8 [E, N, K/4], masks uint8 [E, N, K/8] (paired layouts: the
+    pattern bytes, [E, N, K/16]), scales uint8 [E, N, K/32], global_scale
+    float32 [E].  `layout` is one of the LAYOUT_* constants; a tiled layout has
+    the shapes of its canonical one, bytes arranged as include/moesq.h
+    describes."""
 
     def __init__(self, values, masks, scales, global_scale, layout=LAYOUT_CANONICAL):
         E, N, K4 = values.shape
         self.E, self.N, self.K = int(E), int(N), int(K4) * 4
-        for t, shape, name in [(masks, (E, N, self.K // 8), "masks"),
+        meta = self.K // 16 if layout in PAIRED_LAYOUTS else self.K // 8
+        for t, shape, name in [(masks, (E, N, meta), "masks"),
                                (scales, (E, N, self.K // 32), "scales"),
                                (global_scale, (E,), "global_scale")]:
             if tuple(t.shape) != shape:
@@ -134,13 +141,20 @@ class Weights:
     def nbytes(self) -> int:
         return self.values.numel() + self.masks.numel() + self.scales.numel() + 4 * self.E
 
+    @property
+    def paired(self) -> bool:
+        return self.layout in PAIRED_LAYOUTS
+
     def expert_nbytes(self) -> int:
-        return self.N * self.K * 13 // 32 + 4
+        """Bytes of one expert: 13/32 per weight (4:8 masks) or 11/32 (paired
+        pattern indices: 2.75 bits per weight), plus the fp32 global scale."""
+        return self.N * self.K * (11 if self.paired else 13) // 32 + 4
 
     @staticmethod
     def empty(E: int, N: int, K: int, device="cuda", layout=LAYOUT_CANONICAL):
         u8 = dict(dtype=torch.uint8, device=device)
-        return Weights(torch.empty(E, N, K // 4, **u8), torch.empty(E, N, K // 8, **u8),
+        meta = K // 16 if layout in PAIRED_LAYOUTS else K // 8
+        return Weights(torch.empty(E, N, K // 4, **u8), torch.empty(E, N, meta, **u8),
                        torch.empty(E, N, K // 32, **u8),
                        torch.empty(E, dtype=torch.float32, device=device), layout)
 
@@ -197,6 +211,14 @@ def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, glo
     _check(_pack(_ptr(dense, torch.float32, "dense"), E, N, K, _ptr(values, torch.uint8, "values"),
                  _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
                  _ptr(global_scale, torch.float32, "global_scale"), _stream(stream)))
+
+
+def moesq_pack_weights_paired(dense, E: int, N: int, K: int, values, patterns, scales,
+                              global_scale, stream=None):
+    _check(_pack_paired(_ptr(dense, torch.float32, "dense"), E, N, K,
+                        _ptr(values, torch.uint8, "values"), _ptr(patterns, torch.uint8, "patterns"),
+                        _ptr(scales, torch.uint8, "scales"),
+                        _ptr(global_scale, torch.float32, "global_scale"), _stream(stream)))
 
 
 def moesq_tile_weights(src: Weights, values, masks, scales, stream=None):
@@ -278,18 +300,21 @@ def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):
     return out
 
 
-def pack_weights(dense, stream=None) -> Weights:
-    """dense float32 [E, N, K] on the GPU -> Weights."""
+def pack_weights(dense, stream=None, paired: bool = False) -> Weights:
+    """dense float32 [E, N, K] on the GPU -> canonical (or paired) Weights."""
     E, N, K = dense.shape
-    w = Weights.empty(E, N, K, device=dense.device)
-    moesq_pack_weights(dense, E, N, K, w.values, w.masks, w.scales, w.global_scale, stream)
+    w = Weights.empty(E, N, K, device=dense.device,
+                      layout=LAYOUT_PAIRED if paired else LAYOUT_CANONICAL)
+    pack = moesq_pack_weights_paired if paired else moesq_pack_weights
+    pack(dense, E, N, K, w.values, w.masks, w.scales, w.global_scale, stream)
     return w
 
 
 def tile_weights(w: Weights, stream=None) -> Weights:
-    """Canonical Weights -> a new tiled Weights (shares global_scale)."""
+    """Canonical (paired) Weights -> a new tiled (paired tiled) Weights
+    (shares global_scale)."""
     t = Weights(torch.empty_like(w.values), torch.empty_like(w.masks), torch.empty_like(w.scales),
-                w.global_scale, LAYOUT_TILED)
+                w.global_scale, LAYOUT_PAIRED_TILED if w.paired else LAYOUT_TILED)
     moesq_tile_weights(w, t.values, t.masks, t.scales, stream)
     return t
 

@@ -32,29 +32,39 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def pack_workload(m, wl, proj: int, chunk: int = 16):
+def pack_workload(m, wl, proj: int, chunk: int = 16, paired: bool = False):
     """Dense weights of every expert drawn on the GPU and packed there, a
-    chunk of experts at a time.  Returns the library's Weights."""
+    chunk of experts at a time (4:8, or paired 4:8).  Returns the library's
+    canonical Weights."""
     _, N, K = wl.proj[proj]
-    w = m.Weights.empty(wl.E, N, K)
+    w = m.Weights.empty(wl.E, N, K, layout=m.LAYOUT_PAIRED if paired else m.LAYOUT_CANONICAL)
+    pack = m.moesq_pack_weights_paired if paired else m.moesq_pack_weights
     for c0 in range(0, wl.E, chunk):
         c1 = min(wl.E, c0 + chunk)
         dense = synth.dense_experts(wl, proj, range(c0, c1), device="cuda")
-        m.moesq_pack_weights(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1],
-                             w.scales[c0:c1], w.global_scale[c0:c1])
+        pack(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1], w.scales[c0:c1],
+             w.global_scale[c0:c1])
         del dense
     return w
 
 
-def oracle_expert(wl, proj: int, e: int, device="cuda"):
+def oracle_expert(wl, proj: int, e: int, device="cuda", paired: bool = False):
     """The oracle's compression of the same dense weights (drawn on `device`
     exactly as pack_workload draws them, then moved to the CPU)."""
     dense = synth.dense_expert(wl, proj, e, device=device).cpu().numpy()
-    return oracle.quantize(dense)
+    return oracle.quantize_paired(dense) if paired else oracle.quantize(dense)
 
 
-def assert_same_pack(w, e: int, p: oracle.PackedExpert, what=""):
+def oracle_decode(p, include_global=True):
+    """Dense float64 matrix of an oracle-packed expert of either format."""
+    if isinstance(p, oracle.PackedPairedExpert):
+        return oracle.decode_paired(p, include_global)
+    return oracle.decode(p, include_global)
+
+
+def assert_same_pack(w, e: int, p, what=""):
+    meta = p.patterns if isinstance(p, oracle.PackedPairedExpert) else p.masks
     assert np.array_equal(w.values[e].cpu().numpy(), p.values), f"{what}: values differ"
-    assert np.array_equal(w.masks[e].cpu().numpy(), p.masks), f"{what}: masks differ"
+    assert np.array_equal(w.masks[e].cpu().numpy(), meta), f"{what}: masks/patterns differ"
     assert np.array_equal(w.scales[e].cpu().numpy(), p.scales), f"{what}: scales differ"
     assert w.global_scale[e].item() == float(p.g), f"{what}: global scale differs"

@@ -129,3 +129,29 @@ def test_spgemm_gather_rejects(m):
     assert g(0x10, 0x10, 4, 2, 0x10, ref(_desc(m, layout=7)), 0, 0x10, None, 0, None) == m.ERR_LAYOUT
     assert g(0x10, 0x10, 4, 2, 0x10, d, 5, 0x10, None, 0, None) == m.ERR_ARG         # epilogue
     assert g(None, None, 0, 2, 0x10, d, 0, None, None, 0, None) == m.OK              # T = 0
+
+
+def test_paired_rejects(m):
+    ref = ctypes.byref
+    pp = m._pack_paired
+    assert pp(0x10, 1, 16, 48, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE      # K % 32
+    assert pp(0x10, 0, 16, 64, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE      # E = 0
+    assert pp(0x10, 1, 16, 64, 0x10, None, 0x10, 0x10, None) == m.ERR_NULL       # patterns NULL
+    g = m._spgemm
+    # canonical paired weights must be tiled before the GEMM
+    assert g(0x10, 0x10, 4, ref(_desc(m, layout=m.LAYOUT_PAIRED)), 0, 0x10, None, 0,
+             None) == m.ERR_LAYOUT
+    assert b"tiled first" in m._last_error()
+    # the paired tiled layout needs N % 32 and K % 64
+    assert g(0x10, 0x10, 4, ref(_desc(m, N=48, layout=m.LAYOUT_PAIRED_TILED)), 0, 0x10, None, 0,
+             None) == m.ERR_SHAPE
+    assert g(0x10, 0x10, 4, ref(_desc(m, K=96, layout=m.LAYOUT_PAIRED_TILED)), 0, 0x10, None, 0,
+             None) == m.ERR_SHAPE
+    # tiling takes canonical or paired sources only
+    assert m._tile(ref(_desc(m, layout=m.LAYOUT_PAIRED_TILED)), 0x10, 0x10, 0x10,
+                   None) == m.ERR_LAYOUT
+    assert m._tile(ref(_desc(m, N=48, layout=m.LAYOUT_PAIRED)), 0x10, 0x10, 0x10,
+                   None) == m.ERR_SHAPE
+    assert m._decode(ref(_desc(m, K=96, layout=m.LAYOUT_PAIRED_TILED)), 0, 0x10,
+                     None) == m.ERR_SHAPE
+    assert m._decode(ref(_desc(m, layout=4)), 0, 0x10, None) == m.ERR_LAYOUT

@@ -1,7 +1,7 @@
 """Throughput of the grouped 4:8 sparse-FP4 expert path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep]
+                    [--no-cpu-baseline] [--sweep] [--paired]
 
 One step is one pass of the whole hot path over one batch of synthetic,
 device-resident input:
@@ -23,6 +23,9 @@ prefill workloads, compressed-weight GB/s of the active experts for decode
 workloads.  `roofline` covers the dominant kernel (the first grouped GEMM);
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload.
+
+--paired runs the same step on paired 4:8 weights (two of the four adjacent
+pairs of a group kept, 2.75 bits per weight) through the sparse MFMA.
 """
 from __future__ import annotations
 
@@ -61,6 +64,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of steps: time the first grouped GEMM of --workload over a grid "
                          "of active-expert counts G x rows per expert R (one JSON line per point)")
+    ap.add_argument("--paired", action="store_true",
+                    help="paired 4:8 weights (2.75 bits per weight) on the sparse MFMA instead of "
+                         "the unconstrained 4:8 format")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain gather copy of known size (moesq_unpermute without "
                          "weights over 512 MiB in, 512 MiB out) to scale HBM byte counters")
@@ -82,16 +88,23 @@ def calibrate_copy(m, reps=3):
                       "bytes_written_per_launch": rows * n * 2, "launches": reps}))
 
 
-def pack_on_gpu(m, wl, proj, chunk=16):
-    """Dense weights drawn on the GPU, packed (canonical) and re-laid in the
-    tiled layout the GEMM streams best."""
+def expert_bytes(N, K, paired):
+    """Compressed bytes of one expert: 13/32 byte per weight (4:8 masks) or
+    11/32 (paired pattern indices), plus the fp32 global scale."""
+    return N * K * (11 if paired else 13) // 32 + 4
+
+
+def pack_on_gpu(m, wl, proj, chunk=16, paired=False):
+    """Dense weights drawn on the GPU, packed (canonical, or canonical
+    paired) and re-laid in the tiled layout the GEMM streams best."""
     _, N, K = wl.proj[proj]
-    w = m.Weights.empty(wl.E, N, K)
+    w = m.Weights.empty(wl.E, N, K, layout=m.LAYOUT_PAIRED if paired else m.LAYOUT_CANONICAL)
+    pack = m.moesq_pack_weights_paired if paired else m.moesq_pack_weights
     for c0 in range(0, wl.E, chunk):
         c1 = min(wl.E, c0 + chunk)
         dense = synth.dense_experts(wl, proj, range(c0, c1), device="cuda")
-        m.moesq_pack_weights(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1],
-                             w.scales[c0:c1], w.global_scale[c0:c1])
+        pack(dense, c1 - c0, N, K, w.values[c0:c1], w.masks[c0:c1], w.scales[c0:c1],
+             w.global_scale[c0:c1])
         del dense
     t = m.tile_weights(w)
     torch.cuda.synchronize()
@@ -102,7 +115,7 @@ def pack_on_gpu(m, wl, proj, chunk=16):
 class Step:
     """Buffers and launches of one pass of the hot path."""
 
-    def __init__(self, m, wl, fused=True):
+    def __init__(self, m, wl, fused=True, paired=False):
         self.m, self.wl, self.fused = m, wl, fused
         dev = torch.device("cuda")
         ids, tw = synth.routing(wl)
@@ -110,7 +123,7 @@ class Step:
         self.ids = torch.from_numpy(ids).to(dev)
         self.tw = torch.from_numpy(tw).to(dev)
         self.x = synth.tokens(wl).to(dev)
-        self.w = [pack_on_gpu(m, wl, p) for p in range(len(wl.proj))]
+        self.w = [pack_on_gpu(m, wl, p, paired=paired) for p in range(len(wl.proj))]
         # Weight sets smaller than ~1 GB would stay in the 256 MB Infinity
         # Cache across steps; rotate through replicas so that every step
         # streams its weights from HBM, as a serving step does.
@@ -210,7 +223,8 @@ class Step:
         return res
 
 
-def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launches=16):
+def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launches=16,
+          paired=False):
     """Grouped GEMM of the workload's first projection (plain epilogue) over
     G active experts with R routed rows each, as the pages sweep expert-group
     count x rows per expert.  Each launch reads a different window of G
@@ -219,7 +233,7 @@ def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launc
     `launches` back-to-back launches."""
     _, N, K = wl.proj[0]
     dev = torch.device("cuda")
-    w0 = pack_on_gpu(m, wl, 0)
+    w0 = pack_on_gpu(m, wl, 0, paired=paired)
     reps = [w0] + [m.Weights(w0.values.clone(), w0.masks.clone(), w0.scales.clone(),
                              w0.global_scale.clone(), w0.layout)
                    for _ in range(max(0, -(-ROTATE_BYTES // w0.nbytes) - 1))]
@@ -252,8 +266,9 @@ def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launc
             ev[1].record()
             torch.cuda.synchronize()
             us = 1e3 * ev[0].elapsed_time(ev[1]) / launches
-            wbytes = G * (N * K * 13 // 32 + 4)
-            print(json.dumps({"sweep": wl.name, "N": N, "K": K, "G": G, "R": R, "M": M,
+            wbytes = G * expert_bytes(N, K, paired)
+            print(json.dumps({"sweep": wl.name, "paired": paired, "N": N, "K": K, "G": G, "R": R,
+                              "M": M,
                               "kernel_us": round(us, 2),
                               "weight_GBs": round(wbytes / (us * 1e-6) / 1e9, 1),
                               "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
@@ -262,7 +277,7 @@ def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launc
             del g
 
 
-def measured_traffic(workload, proj_name):
+def measured_traffic(workload, proj_name, paired=False):
     """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
     counter summary, or None when the GEMM source has changed since the
     counters were taken (or no summary covers this workload)."""
@@ -276,11 +291,11 @@ def measured_traffic(workload, proj_name):
     src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in ("spgemm.hip", "common.hpp"))
     if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
         return None
-    k = rec.get("kernels", {}).get(f"{workload}/{proj_name}")
+    k = rec.get("kernels", {}).get(f"{workload}/{proj_name}" + ("/paired" if paired else ""))
     return None if k is None else k.get("traffic_bytes")
 
 
-def gemm_work(wl, ids):
+def gemm_work(wl, ids, paired=False):
     """Dense-equivalent flops and compressed weight bytes of the active
     experts, per projection."""
     counts = np.bincount(ids, minlength=wl.E)
@@ -288,7 +303,7 @@ def gemm_work(wl, ids):
     res = []
     for _, N, K in wl.proj:
         flops = 2.0 * wl.M * N * K
-        wbytes = active * (N * K * 13 // 32 + 4)
+        wbytes = active * expert_bytes(N, K, paired)
         res.append((flops, wbytes))
     return res, active
 
@@ -303,7 +318,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_baseline(wl, budget_s, paired=False):
     """The CPU oracle on the same workload, each phase timed on its own.
 
     Route, permute and the combine run on the whole workload (data movement;
@@ -341,7 +356,7 @@ def cpu_baseline(wl, budget_s):
     active = int((counts > 0).sum())
     order = np.argsort(-counts, kind="stable")
     flops_all = sum(2.0 * wl.M * N * K for _, N, K in wl.proj)
-    bytes_all = sum(active * (N * K * 13 // 32 + 4) for _, N, K in wl.proj)
+    bytes_all = sum(active * expert_bytes(N, K, paired) for _, N, K in wl.proj)
     t0 = time.perf_counter()
     flops = 0.0
     wbytes = 0
@@ -354,10 +369,10 @@ def cpu_baseline(wl, budget_s):
         for p, (_, N, K) in enumerate(wl.proj):
             dense = synth.dense_expert(wl, p, int(e)).numpy()
             t = time.perf_counter()
-            pk = oracle.quantize(dense)
+            pk = oracle.quantize_paired(dense) if paired else oracle.quantize(dense)
             ph["compress"] += time.perf_counter() - t
             t = time.perf_counter()
-            Wd = oracle.decode(pk)
+            Wd = oracle.decode_paired(pk) if paired else oracle.decode(pk)
             ph["decode"] += time.perf_counter() - t
             t = time.perf_counter()
             y = oracle.expert_gemm(a, Wd)
@@ -395,9 +410,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     if args.sweep:
-        sweep(m, wl)
+        sweep(m, wl, paired=args.paired)
         return
-    step = Step(m, wl, fused=not args.unfused)
+    step = Step(m, wl, fused=not args.unfused, paired=args.paired)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -417,7 +432,7 @@ def main():
     ms_step = 1e3 * wall / args.steps
     kernel_ms = step.kernel_ms(reps=max(8, len(step.replicas)))
 
-    work, active = gemm_work(wl, step.ids_host)
+    work, active = gemm_work(wl, step.ids_host, args.paired)
     total_flops = sum(f for f, _ in work)
     total_wbytes = sum(b for _, b in work)
     prefill = wl.M >= 4096
@@ -433,18 +448,21 @@ def main():
                 "unit": "TFLOP/s"}
         # MFMAs the kernel executes: each expert's rows padded to whole
         # 32-row token fragments (the prefill tile); one MAC per kept weight
-        # is the useful rate
+        # is the useful rate.  Paired weights run on the sparse MFMA, whose
+        # pipe retires twice the dense-equivalent work of the dense MFMA.
         _, N0, K0 = wl.proj[0]
         counts = np.bincount(step.ids_host, minlength=wl.E)
         padded = float((-(-counts // 32) * 32).sum())
+        pipe_peak = PEAK_BF16_TFLOPS * (2 if args.paired else 1)
         roof["mfma_executed_tflops"] = 2.0 * padded * N0 * K0 / (g0_ms * 1e-3) / 1e12
-        roof["mfma_executed_frac"] = roof["mfma_executed_tflops"] / PEAK_BF16_TFLOPS
+        roof["mfma_executed_frac"] = roof["mfma_executed_tflops"] / pipe_peak
+        roof["mfma_pipe_peak"] = pipe_peak
         roof["useful_tflops"] = 0.5 * roof["achieved"]
     else:
         roof = {"bound": "hbm", "achieved": b0 / (g0_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name, wl.proj[0][0])
+    roof["traffic"] = measured_traffic(wl.name, wl.proj[0][0], args.paired)
     roof["kernel"] = f"moesq_grouped_spgemm ({wl.proj[0][0]})"
     roof["kernel_ms"] = g0_ms
 
@@ -453,14 +471,15 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "E": wl.E, "T": wl.T, "k": wl.k, "routed_rows": wl.M,
                       "projections": [list(p) for p in wl.proj], "routing": wl.bias,
-                      "active_experts": active, "parallelism": "none"},
+                      "active_experts": active, "parallelism": "none",
+                      "weights": "paired 4:8 (2.75 bpw)" if args.paired else "4:8 (3.25 bpw)"},
            "kernel_ms": kernel_ms,
            "weight_replicas": len(step.replicas),
            "gemm_tflops_dense_equiv": total_flops / 1e12,
            "weight_gb_active": total_wbytes / 1e9,
            "roofline": roof}
     if not args.no_cpu_baseline:
-        work, dt, threads, sample, phases = cpu_baseline(wl, args.cpu_seconds)
+        work, dt, threads, sample, phases = cpu_baseline(wl, args.cpu_seconds, args.paired)
         cv = work / dt / 1e12 if prefill else work / dt / 1e9
         res["cpu_baseline"] = {"value": cv, "unit": unit, "cores": threads, "kind": "oracle",
                                "sample": sample, "seconds_full_step": dt, "phases_s": phases,

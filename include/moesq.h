@@ -195,7 +195,8 @@ moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, 
  *   ws, ws_bytes    workspace; moesq_spgemm_workspace_bytes() bytes (may be 0)
  * Rows of y outside every expert range are not written.
  * Limits: K % 32 == 0, N % 16 == 0 (SWIGLU: N % 32 == 0), E <= MOESQ_MAX_EXPERTS,
- *         M >= 0, N*K/4 < 2^31 (one expert's values under 2 GiB).
+ *         M >= 0, N*K/4 < 2^31 (one expert's values under 2 GiB),
+ *         M*K < 2^31 (x_routed under 4 GiB).
  */
 moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed, const int32_t *expert_offsets,
                                     int32_t M, const moesq_weights_t *w, int32_t epilogue,
@@ -212,7 +213,8 @@ size_t moesq_spgemm_workspace_bytes(int32_t M, const moesq_weights_t *w);
  *   x        [T][K] bf16 tokens;  perm [T*k] int32 (moesq_route output)
  *   expert_offsets, w, epilogue, y, ws, ws_bytes: as moesq_grouped_spgemm,
  *   with M = T*k.  Rows r whose perm[r] is outside [0, T*k) come out zero.
- * Limits: those of moesq_grouped_spgemm; T >= 0, k >= 1, T*k < 2^31.
+ * Limits: those of moesq_grouped_spgemm, with T*K < 2^31 in place of M*K;
+ *         T >= 0, k >= 1, T*k < 2^31.
  */
 moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const int32_t *perm, int32_t T,
                                            int32_t k, const int32_t *expert_offsets,

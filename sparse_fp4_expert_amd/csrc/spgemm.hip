@@ -333,6 +333,27 @@ __device__ __forceinline__ void mma_chunk_paired(typename Smfmac<MS>::C (&acc)[R
   }
 }
 
+// LDS pointer / 32-bit LDS address of a __shared__ object (device only: the
+// address space does not exist on the host).
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(void *p) {
+  return (__attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// SIZE bytes per lane from a buffer to LDS at lds + SIZE * lane.
+template <int SIZE>
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff,
+                                              uint32_t soff) {
+  static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "LDS DMA of 2, 4 or 16 bytes per lane");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
+  else if constexpr (SIZE == 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 4, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 2, voff, soff, 0, 0);
+}
+
 // Weight formats of the kernel.
 enum { FMT_CANONICAL = 0, FMT_TILED = 1, FMT_PAIRED = 2 };
 
@@ -359,10 +380,25 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
 
   __shared__ uint4 lut[256];
-  __shared__ int s_lo[MOESQ_MAX_EXPERTS + 1];
   __shared__ int s_item[MOESQ_MAX_EXPERTS + 1];
   __shared__ __attribute__((aligned(1024))) uint16_t tkA[BM * KC];
   __shared__ __attribute__((aligned(1024))) uint16_t tkB[BM * KC];
+  // Contraction tile on paired weights: the weights of chunk c + 2 stream
+  // into a three-slot LDS ring by direct-to-LDS buffer loads while chunk c
+  // computes, so each weight load has two chunks of compute to land in; the
+  // tokens stay one chunk ahead.  (The sparse MFMA halves the compute per
+  // chunk, which one chunk of prefetch no longer covers.  The 4:8 tile keeps
+  // its weights in registers: its decode already loads LDS with the
+  // selector table, and measured slower with the ring.)  Per slot, wave and
+  // fragment: the 64 lanes' 16 value bytes, their mask (8) or window (4)
+  // bytes and 2 scale bytes, in lane order.
+  constexpr bool RING = PAIRED && MS == 32;
+  // (a 2-byte direct-to-LDS load fills a 4-byte slot per lane)
+  constexpr int RV = 64 * 16, RM = 64 * (PAIRED ? 4 : 8), RS = 64 * 4;
+  constexpr int RFB = RV + RM + RS;                 // bytes per fragment
+  constexpr int RSLOT = WAVES * RF * RFB;           // bytes per slot
+  constexpr int RING_LOADS = RF * (PAIRED ? 3 : 4); // buffer loads per wave per slot
+  __shared__ __attribute__((aligned(16))) uint8_t wring[RING ? 3 * RSLOT : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -370,14 +406,16 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   const int E = a.E, N = a.N, K = a.K, M = a.M;
 
   if constexpr (!PAIRED) build_group_lut(lut);
-  for (int e = tid; e <= E; e += WAVES * 64) s_lo[e] = min(max(a.offsets[e], 0), M);
+  // expert row ranges straight from the offsets (clamped to [0, M]); only
+  // the item prefix is kept in LDS
+  auto off_at = [&](int e) { return min(max(a.offsets[e], 0), M); };
   __syncthreads();
   if (wave == 0) {
     // items per expert and their exclusive prefix, by one wave
     const int per = (E + 63) / 64;
     const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
     int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += (max(0, s_lo[e + 1] - s_lo[e]) + BM - 1) / BM;
+    for (int e = e0; e < e1; ++e) sum += (max(0, off_at(e + 1) - off_at(e)) + BM - 1) / BM;
     int incl = sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -387,7 +425,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     int run = incl - sum;
     for (int e = e0; e < e1; ++e) {
       s_item[e] = run * a.row_tiles;
-      run += (max(0, s_lo[e + 1] - s_lo[e]) + BM - 1) / BM;
+      run += (max(0, off_at(e + 1) - off_at(e)) + BM - 1) / BM;
     }
     if (lane == 63) s_item[E] = incl * a.row_tiles;
   }
@@ -427,7 +465,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     const int e = lo;
     const int local = item - s_item[e];
     const int tt = local / a.row_tiles, rt = local - tt * a.row_tiles;
-    const int e_lo = s_lo[e], e_hi = max(e_lo, s_lo[e + 1]);
+    const int e_lo = off_at(e), e_hi = max(e_lo, off_at(e + 1));
     const int tok0 = e_lo + tt * BM;
     const int ntok = min(BM, e_hi - tok0);
     const int nft = (ntok + MS - 1) / MS;
@@ -496,7 +534,9 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     // fused into the GEMM; an out-of-range entry reads token 0 and its
     // output row is written as zero, as a zero routed row would give).
     const int nrows = nft * MS;
-    const uint16_t *srow[BPW];
+    // element offsets from x (under 2^31: checked on the host), so that the
+    // loads take x as a scalar base and a 32-bit lane offset
+    uint32_t srow[BPW];
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       const int r = tok0 + min((wave * BPW + j) * (64 / UPR) + lane / UPR, ntok - 1);
@@ -505,7 +545,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         const int pi = a.perm[r];
         src = (pi >= 0 && pi < a.T * a.k) ? pi / a.k : 0;
       }
-      srow[j] = a.x + (size_t)src * K;
+      srow[j] = (uint32_t)src * (uint32_t)K;
     }
     auto load_tok = [&](uint16_t *buf, int k0) {
 #pragma unroll
@@ -515,7 +555,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         const int c = (lane % UPR) ^ (row % UPR);
         const int kk = min(k0 + c * 8, K - 8);
         __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void *)(srow[j] + kk),
+            (__attribute__((address_space(1))) void *)(a.x + (srow[j] + (uint32_t)kk)),
             (__attribute__((address_space(3))) void *)(buf + (wave * BPW + j) * 512), 16, 0, 0);
       }
     };
@@ -535,17 +575,23 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         if ((wave * BPW + j) * (64 / UPR) >= nrows) break;   // block never loaded
-        uint16_t *blk = buf + (wave * BPW + j) * 512;
-        const uint4 x = *reinterpret_cast<const uint4 *>(blk + 8 * lane);
-        const uint4 y = *reinterpret_cast<const uint4 *>(blk + 8 * (lane ^ 1));
+        // LDS accesses in asm with their own waits: the waitcnt pass cannot
+        // tell this buffer from the weight ring still streaming in, and
+        // would wait for the ring's loads (vmcnt) before these writes
+        const uint32_t blk = lds_addr(buf + (wave * BPW + j) * 512);
+        const uint32_t a_own = blk + 16u * lane, a_nbr = blk + 16u * (lane ^ 1);
+        u32x4_t x, y;
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(x), "=&v"(y) : "v"(a_own), "v"(a_nbr) : "memory");
         // own group: dwords p0 p1; the neighbour's: p2 p3; G goes first
-        uint2 own, nbr;
-        own.x = __builtin_amdgcn_perm(x.y, x.x, split_sel);
-        own.y = __builtin_amdgcn_perm(x.w, x.z, split_sel);
-        nbr.x = __builtin_amdgcn_perm(y.y, y.x, split_sel);
-        nbr.y = __builtin_amdgcn_perm(y.w, y.z, split_sel);
-        *reinterpret_cast<uint2 *>(blk + 8 * lane + 4 * split_h) = own;
-        *reinterpret_cast<uint2 *>(blk + 8 * lane + 4 * (split_h ^ 1)) = nbr;
+        u32x2_t own, nbr;
+        own[0] = __builtin_amdgcn_perm(x[1], x[0], split_sel);
+        own[1] = __builtin_amdgcn_perm(x[3], x[2], split_sel);
+        nbr[0] = __builtin_amdgcn_perm(y[1], y[0], split_sel);
+        nbr[1] = __builtin_amdgcn_perm(y[3], y[2], split_sel);
+        asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3\n\ts_waitcnt lgkmcnt(0)"
+                     :: "v"(a_own + 8u * split_h), "v"(own), "v"(a_own + 8u * (split_h ^ 1)), "v"(nbr)
+                     : "memory");
       }
     };
     // tiled: this lane's segment of the chunk at k0, clamped into K
@@ -583,7 +629,113 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           load_wchunk(w, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
         }
       };
-      if constexpr (PAIRED) {
+      if constexpr (RING) {
+        auto ring_load = [&](int slot, int k0) {
+          const uint32_t lo = tlo(k0);
+          uint8_t *base = wring + slot * RSLOT + wave * (RF * RFB);
+#pragma unroll
+          for (int f = 0; f < RF; ++f) {
+            uint8_t *fb = base + f * RFB;
+            buffer_to_lds<16>(vr, fb, lo, fv[f]);
+            if constexpr (PAIRED) {
+              buffer_to_lds<4>(mr, fb + RV, lo >> 2, fm[f]);
+            } else {
+              buffer_to_lds<4>(mr, fb + RV, lo >> 1, fm[f]);
+              buffer_to_lds<4>(mr, fb + RV + 256, (lo >> 1) + 4, fm[f]);
+            }
+            buffer_to_lds<2>(sr, fb + RV + RM, lo >> 3, fs[f]);
+          }
+        };
+        // The ring is read with one asm block per fragment that waits for its
+        // own reads (lgkmcnt): the waitcnt pass would otherwise make every
+        // read of the ring wait for the slot still streaming in (vmcnt).
+        const uint32_t ring0 = lds_addr(wring) + (uint32_t)(wave * (RF * RFB));
+        using WC = std::conditional_t<PAIRED, PChunk<RF>, WChunk<RF, KQ>>;
+        auto ring_read = [&](WC &w, int slot) {
+#pragma unroll
+          for (int f = 0; f < RF; ++f) {
+            const uint32_t fb = ring0 + (uint32_t)(slot * RSLOT + f * RFB);
+            const uint32_t av = fb + lane * 16, am = fb + RV + lane * 4, as = fb + RV + RM + lane * 4;
+            u32x4_t v;
+            uint32_t m0, m1 = 0, sc;
+            if constexpr (PAIRED) {
+              asm volatile("ds_read_b128 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_u16 %2, %5\n\t"
+                           "s_waitcnt lgkmcnt(0)"
+                           : "=&v"(v), "=&v"(m0), "=&v"(sc) : "v"(av), "v"(am), "v"(as) : "memory");
+              w.w[f] = m0;
+            } else {
+              asm volatile("ds_read_b128 %0, %4\n\tds_read_b32 %1, %5\n\t"
+                           "ds_read_b32 %2, %5 offset:256\n\tds_read_u16 %3, %6\n\t"
+                           "s_waitcnt lgkmcnt(0)"
+                           : "=&v"(v), "=&v"(m0), "=&v"(m1), "=&v"(sc)
+                           : "v"(av), "v"(am), "v"(as) : "memory");
+              w.m[f][0] = m0;
+              w.m[f][1] = m1;
+            }
+            w.v[f][0] = v[0];
+            w.v[f][1] = v[1];
+            w.v[f][2] = v[2];
+            w.v[f][3] = v[3];
+            w.s[f] = sc;
+          }
+        };
+        ring_load(0, 0);
+        if (nk > 1) ring_load(1, KC);
+        load_tok(tkA, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (PAIRED) split_tok(tkA);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        // One chunk: tokens of c + 1 and weights of c + 2 are issued in that
+        // order, so waiting for all but the last RING_LOADS loads lands the
+        // tokens (and, being older, the weights of c + 1) and leaves the
+        // weights of c + 2 in flight.  A bare barrier: every LDS write this
+        // chunk makes (split, ring) is covered by the explicit waits.
+        auto chunk = [&](int c, int slot, const uint16_t *cur, uint16_t *nxt) {
+          if (c + 1 < nk) load_tok(nxt, (c + 1) * KC);
+          if (c + 2 < nk) ring_load(slot == 0 ? 2 : slot - 1, (c + 2) * KC);
+          WC wc;
+          ring_read(wc, slot);
+          if ((c + 1) * KC > K) {
+            // segments past K were clamped to the last one: clear their
+            // masks (4:8) or codes (paired)
+            const bool ok = (uint32_t)((c * KC) >> 6) + (uint32_t)q < segs;
+#pragma unroll
+            for (int f = 0; f < RF; ++f) {
+              if constexpr (PAIRED) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wc.v[f][i] = ok ? wc.v[f][i] : 0u;
+              } else {
+#pragma unroll
+                for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) wc.m[f][i] = ok ? wc.m[f][i] : 0u;
+              }
+            }
+          }
+          if constexpr (PAIRED)
+            mma_chunk_paired<MS, RF, TF, KC, FULL>(acc, cur, wc, nft, q, rl);
+          else
+            mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
+          if (c + 2 < nk)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING_LOADS) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (PAIRED)
+            if (c + 1 < nk) split_tok(nxt);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+        };
+        // slots cycle 0,1,2 and token buffers A,B: unrolled over the chunk
+        // pair, the slot advances at run time
+        int slot = 0;
+        for (int c = 0; c < nk; c += 2) {
+          chunk(c, slot, tkA, tkB);
+          slot = slot == 2 ? 0 : slot + 1;
+          if (c + 1 < nk) {
+            chunk(c + 1, slot, tkB, tkA);
+            slot = slot == 2 ? 0 : slot + 1;
+          }
+        }
+      } else if constexpr (PAIRED) {
         PChunk<RF> wA, wB;
         load_pchunk(wA, vr, mr, sr, fv, fm, fs, tlo(0));
         load_tok(tkA, 0);
@@ -693,7 +845,11 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         }
       }
     };
-    if (nft == TF)
+    // The ring tile runs partial token tiles as full ones: fragments past
+    // the routed rows compute on stale LDS rows whose outputs are never
+    // stored, which keeps the accumulators free of branches (with them the
+    // tile spills).
+    if (RING || nft == TF)
       run_item(std::true_type{});
     else
       run_item(std::false_type{});
@@ -803,6 +959,9 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   if (!expert_offsets) return fail(MOESQ_ERR_NULL, std::string(who) + ": expert_offsets is NULL");
   if (M == 0) return MOESQ_OK;
   if (!x || !y) return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL input or output rows");
+  // token rows are addressed by 32-bit element offsets
+  if ((long long)(perm ? T : M) * w->K > 0x7fffffffll)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": rows of x times K must stay under 2^31");
   SpgemmArgs a{};
   a.x = x;
   a.perm = perm;

@@ -11,9 +11,10 @@
 //
 // Work decomposition.  An item is (expert e, token tile of up to BM routed
 // rows, row tile of BN weight rows).  Every workgroup reads the expert
-// offsets into LDS, forms the per-expert item counts and their prefix, and
-// walks the items with a grid-sized stride, so the grid never depends on the
-// routing, which only the device knows.  Token tiles are trimmed to whole
+// offsets, forms the item list in LDS -- all whole token tiles first, then
+// the partial ones by descending size, so that rounds of workgroups take
+// the costly items first -- and walks the items with a grid-sized stride,
+// so the grid never depends on the routing, which only the device knows.  Token tiles are trimmed to whole
 // MFMA fragments, so an expert with few rows costs few MFMAs and mostly
 // streams its weights.
 //
@@ -380,7 +381,14 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
 
   __shared__ uint4 lut[256];
-  __shared__ int s_item[MOESQ_MAX_EXPERTS + 1];
+  // Item order: every expert's whole token tiles first (expert order), then
+  // the partial tiles (at most one per expert) by descending fragment count.
+  // Workgroups take items in fixed rounds, so putting the costly items first
+  // and the cheap ones last balances the rounds (longest job first).
+  __shared__ int s_full[MOESQ_MAX_EXPERTS + 1];   // item prefix of the whole tiles
+  __shared__ int s_part[MOESQ_MAX_EXPERTS];       // experts with a partial tile, costly first
+  __shared__ int s_npart;
+  __shared__ int s_cnt[MOESQ_MAX_EXPERTS];        // routed rows per expert
   __shared__ __attribute__((aligned(1024))) uint16_t tkA[BM * KC];
   __shared__ __attribute__((aligned(1024))) uint16_t tkB[BM * KC];
   // Contraction tile on paired weights: the weights of chunk c + 2 stream
@@ -409,28 +417,49 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   // expert row ranges straight from the offsets (clamped to [0, M]); only
   // the item prefix is kept in LDS
   auto off_at = [&](int e) { return min(max(a.offsets[e], 0), M); };
+  for (int e = tid; e < E; e += WAVES * 64) s_cnt[e] = max(0, off_at(e + 1) - off_at(e));
   __syncthreads();
   if (wave == 0) {
-    // items per expert and their exclusive prefix, by one wave
+    // by one wave: prefix of the whole tiles, then the partial tiles bucketed
+    // by fragment count (TF down to 1), experts ascending within a bucket
     const int per = (E + 63) / 64;
     const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-    int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += (max(0, off_at(e + 1) - off_at(e)) + BM - 1) / BM;
-    int incl = sum;
+    auto scan = [&](int v) {   // inclusive prefix over the wave
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += t;
-    }
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d, 64);
+        if (lane >= d) v += t;
+      }
+      return v;
+    };
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += s_cnt[e] / BM;
+    const int incl = scan(sum);
     int run = incl - sum;
     for (int e = e0; e < e1; ++e) {
-      s_item[e] = run * a.row_tiles;
-      run += (max(0, off_at(e + 1) - off_at(e)) + BM - 1) / BM;
+      s_full[e] = run * a.row_tiles;
+      run += s_cnt[e] / BM;
     }
-    if (lane == 63) s_item[E] = incl * a.row_tiles;
+    if (lane == 63) s_full[E] = incl * a.row_tiles;
+    int base = 0;
+    for (int c = TF; c >= 1; --c) {
+      auto cls = [&](int e) {
+        const int rem = s_cnt[e] % BM;
+        return rem > 0 && (rem + MS - 1) / MS == c;
+      };
+      int cnt = 0;
+      for (int e = e0; e < e1; ++e) cnt += cls(e);
+      const int ci = scan(cnt);
+      int pos = base + ci - cnt;
+      for (int e = e0; e < e1; ++e)
+        if (cls(e)) s_part[pos++] = e;
+      base += __shfl(ci, 63, 64);
+    }
+    if (lane == 0) s_npart = base;
   }
   __syncthreads();
-  const int total = s_item[E];
+  const int nfull = s_full[E];
+  const int total = nfull + s_npart * a.row_tiles;
 
   const int q = lane / MS;     // lane group: K range [k0 + KQ*q, +KQ) of a chunk
   const int rl = lane % MS;    // A-fragment row / B-fragment token of this lane
@@ -457,14 +486,23 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     const int per = (n_round + 7) >> 3;
     if (wg_in_xcd >= per || xcd * per + wg_in_xcd >= n_round) break;   // no item in the last round
     const int item = base + xcd * per + wg_in_xcd;
-    int lo = 0, hi = E;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_item[mid] <= item) lo = mid; else hi = mid - 1;
+    int e, tt, rt;
+    if (item < nfull) {
+      int lo = 0, hi = E;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_full[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      const int local = item - s_full[e];
+      tt = local / a.row_tiles;
+      rt = local - tt * a.row_tiles;
+    } else {
+      const int j = (item - nfull) / a.row_tiles;
+      rt = item - nfull - j * a.row_tiles;
+      e = s_part[j];
+      tt = s_cnt[e] / BM;   // the last, partial tile
     }
-    const int e = lo;
-    const int local = item - s_item[e];
-    const int tt = local / a.row_tiles, rt = local - tt * a.row_tiles;
     const int e_lo = off_at(e), e_hi = max(e_lo, off_at(e + 1));
     const int tok0 = e_lo + tt * BM;
     const int ntok = min(BM, e_hi - tok0);

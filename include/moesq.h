@@ -316,6 +316,21 @@ moesq_status_t moesq_validate(const int32_t *topk_ids, int32_t T, int32_t k, int
                               const int32_t *expert_offsets, const moesq_weights_t *w,
                               uint64_t *counts, hipStream_t stream);
 
+/*
+ * moesq_stream_read — measurement utility, not a step of the MoE path.
+ * Reads `bytes` of device memory at `buf` once, in 16-byte loads with eight
+ * in flight per lane, and writes nothing of use: the rate it reaches is the
+ * practical HBM read ceiling against which the decode GEMMs (weight streams)
+ * are compared, beside the device's published pin rate.
+ *   buf [bytes] device, 16-byte aligned; bytes a multiple of 16 (0 is a no-op)
+ *   sink [1]   device uint32, written only in a case that cannot occur for
+ *              ordinary data (keeps the loads from being dropped); caller-owned.
+ * Returns MOESQ_ERR_NULL / MOESQ_ERR_ARG for bad arguments, MOESQ_ERR_HIP if
+ * the launch fails.  Asynchronous on `stream`.
+ */
+moesq_status_t moesq_stream_read(const void *buf, size_t bytes, uint32_t *sink,
+                                 hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *moesq_status_string(moesq_status_t st);
 /* Detail of the last error returned on the calling thread ("" if none). */

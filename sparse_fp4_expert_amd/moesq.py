@@ -60,6 +60,7 @@ _decode = _sig("moesq_decode_weights", _i32, ctypes.POINTER(WeightsDesc), _i32, 
 _tile = _sig("moesq_tile_weights", _i32, ctypes.POINTER(WeightsDesc), _vp, _vp, _vp, _vp)
 _validate = _sig("moesq_validate", _i32, _vp, _i32, _i32, _i32, _vp, ctypes.POINTER(WeightsDesc),
                  ctypes.POINTER(ctypes.c_uint64), _vp)
+_stream_read = _sig("moesq_stream_read", _i32, _vp, _sz, _vp, _vp)
 _status_string = _sig("moesq_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moesq_last_error", ctypes.c_char_p)
 _version = _sig("moesq_version", _i32)
@@ -69,7 +70,7 @@ EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
             "moesq_grouped_spgemm_gather", "moesq_unpermute",
             "moesq_pack_weights", "moesq_pack_weights_paired", "moesq_tile_weights",
             "moesq_decode_weights",
-            "moesq_validate", "moesq_status_string",
+            "moesq_validate", "moesq_stream_read", "moesq_status_string",
             "moesq_last_error", "moesq_version"]
 
 
@@ -247,6 +248,13 @@ def moesq_validate(topk_ids=None, T: int = 0, k: int = 1, E: int = 1, expert_off
     if st != ERR_ARG:
         _check(st)
     return dict(zip(VALIDATE_CHECKS, (int(c) for c in counts)))
+
+
+def moesq_stream_read(buf, sink, stream=None):
+    """Measurement utility: one streaming read of the uint8 device tensor
+    `buf` (the practical HBM read ceiling); `sink` is a 1-element int32 tensor."""
+    _check(_stream_read(_ptr(buf, torch.uint8, "buf"), buf.numel(),
+                        _ptr(sink, torch.int32, "sink"), _stream(stream)))
 
 
 # ------------------------------------------------------------ helpers (allocate with torch)

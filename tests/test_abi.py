@@ -155,3 +155,12 @@ def test_paired_rejects(m):
     assert m._decode(ref(_desc(m, K=96, layout=m.LAYOUT_PAIRED_TILED)), 0, 0x10,
                      None) == m.ERR_SHAPE
     assert m._decode(ref(_desc(m, layout=4)), 0, 0x10, None) == m.ERR_LAYOUT
+
+
+def test_stream_read_rejects(m):
+    sr = m._stream_read
+    assert sr(None, 16, 0x10, None) == m.ERR_NULL
+    assert sr(0x10, 16, None, None) == m.ERR_NULL
+    assert sr(0x10, 24, 0x10, None) == m.ERR_ARG      # bytes % 16
+    assert sr(0x18, 16, 0x10, None) == m.ERR_ARG      # misaligned buffer
+    assert sr(0x10, 0, 0x10, None) == m.OK            # nothing to read

@@ -57,3 +57,16 @@ def test_validate_counts_planted_violations(lib, tiled):
     detail = m._last_error().decode()
     for word in ("ids", "offset", "masks", "scale", "global"):
         assert word in detail, detail
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000 + 16 * 7, 64 << 20])
+def test_stream_read_runs(lib, nbytes):
+    """The measurement read leaves the sink alone for data whose word XOR is
+    not its marker (all-ones bytes XOR to 0 or 0x01010101), at ragged sizes."""
+    m = lib
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    m.moesq_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0

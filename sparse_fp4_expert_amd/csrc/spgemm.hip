@@ -358,9 +358,15 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, void *ld
 // Weight formats of the kernel.
 enum { FMT_CANONICAL = 0, FMT_TILED = 1, FMT_PAIRED = 2 };
 
+// Dynamic LDS of the item schedule for E experts: prefix [E+1] and row
+// counts [E] as int, partial-tile experts [E] as uint16, rounded to 16 bytes.
+static inline size_t spgemm_sched_bytes(int E) {
+  return ((size_t)(2 * E + 1) * 4 + (size_t)E * 2 + 15) & ~(size_t)15;
+}
+
 template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(WAVES * 64)
-// 16-row tiles stream weights: at most 128 VGPRs, so that two 8-wave
+// 16-row tiles stream weights: at most 128 VGPRs, so that four 4-wave
 // workgroups share a CU.  32-row tiles hold 128 accumulators per lane.
 __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void spgemm_kernel(
     SpgemmArgs a) {
@@ -380,15 +386,16 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   static_assert(KQ == 32 || KQ == 64, "a lane group covers one or two scale blocks");
   static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
 
-  __shared__ uint4 lut[256];
+  __shared__ uint4 lut[PAIRED ? 1 : 256];   // 4:8 selector table (paired needs none)
   // Item order: every expert's whole token tiles first (expert order), then
   // the partial tiles (at most one per expert) by descending fragment count.
   // Workgroups take items in fixed rounds, so putting the costly items first
   // and the cheap ones last balances the rounds (longest job first).
-  __shared__ int s_full[MOESQ_MAX_EXPERTS + 1];   // item prefix of the whole tiles
-  __shared__ int s_part[MOESQ_MAX_EXPERTS];       // experts with a partial tile, costly first
+  // The three per-expert arrays sit in dynamic LDS sized for the launch's
+  // E (spgemm_sched_bytes), so that a small expert count leaves room for
+  // more workgroups per CU.
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
   __shared__ int s_npart;
-  __shared__ int s_cnt[MOESQ_MAX_EXPERTS];        // routed rows per expert
   __shared__ __attribute__((aligned(1024))) uint16_t tkA[BM * KC];
   __shared__ __attribute__((aligned(1024))) uint16_t tkB[BM * KC];
   // Contraction tile on paired weights: the weights of chunk c + 2 stream
@@ -412,6 +419,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.E, N = a.N, K = a.K, M = a.M;
+  int *const s_full = s_dyn;                  // [E+1] item prefix of the whole tiles
+  int *const s_cnt = s_dyn + E + 1;           // [E] routed rows per expert
+  uint16_t *const s_part = reinterpret_cast<uint16_t *>(s_dyn + 2 * E + 1);
+                                              // [E] experts with a partial tile, costly first
 
   if constexpr (!PAIRED) build_group_lut(lut);
   // expert row ranges straight from the offsets (clamped to [0, M]); only
@@ -561,6 +572,57 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       }
     };
 
+    // tiled: this lane's segment of the chunk at k0, clamped into K
+    auto tlo = [&](int k0) {
+      const uint32_t seg = min((uint32_t)(k0 >> 6) + (uint32_t)q, segs - 1u);
+      return seg * 512u + (uint32_t)rl * 16u;
+    };
+    auto wok = [&](int k0, bool (&ok)[RF]) {
+#pragma unroll
+      for (int f = 0; f < RF; ++f) ok[f] = fval[f] && (k0 + KQ * q < K);
+      return k0 + KQ * q + KQ <= K;
+    };
+    auto load_w = [&](WChunk<RF, KQ> &w, int k0) {
+      if constexpr (TILED) {
+        load_wchunk_tiled(w, vr, mr, sr, fv, fm, fs, tlo(k0));
+      } else {
+        bool ok[RF];
+        const bool whole = wok(k0, ok);
+        uint32_t kv, km, ks;
+        koff(k0, kv, km, ks);
+        load_wchunk(w, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
+      }
+    };
+    auto ring_load = [&](int slot, int k0) {
+      const uint32_t lo = tlo(k0);
+      uint8_t *base = wring + slot * RSLOT + wave * (RF * RFB);
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        uint8_t *fb = base + f * RFB;
+        buffer_to_lds<16>(vr, fb, lo, fv[f]);
+        if constexpr (PAIRED) {
+          buffer_to_lds<4>(mr, fb + RV, lo >> 2, fm[f]);
+        } else {
+          buffer_to_lds<4>(mr, fb + RV, lo >> 1, fm[f]);
+          buffer_to_lds<4>(mr, fb + RV + 256, (lo >> 1) + 4, fm[f]);
+        }
+        buffer_to_lds<2>(sr, fb + RV + RM, lo >> 3, fs[f]);
+      }
+    };
+    // The item's first weight chunk is issued before the gather offsets
+    // below (a dependent load), so that the two latencies overlap.  The
+    // previous item ended on a barrier: the ring slots and registers are free.
+    using FirstChunk = std::conditional_t<PAIRED, PChunk<RF>, WChunk<RF, KQ>>;
+    FirstChunk w0;
+    if constexpr (RING) {
+      ring_load(0, 0);
+      if (nk > 1) ring_load(1, KC);
+    } else if constexpr (PAIRED) {
+      load_pchunk(w0, vr, mr, sr, fv, fm, fs, tlo(0));
+    } else {
+      load_w(w0, 0);
+    }
+
     // Token tile of a chunk: each 1 KB direct-to-LDS load of this wave
     // covers 64/UPR token rows; lane L fetches unit (L % UPR) ^ (row % UPR)
     // of its row, so that it lands in the swizzled slot mma_chunk reads.
@@ -632,16 +694,6 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
                      : "memory");
       }
     };
-    // tiled: this lane's segment of the chunk at k0, clamped into K
-    auto tlo = [&](int k0) {
-      const uint32_t seg = min((uint32_t)(k0 >> 6) + (uint32_t)q, segs - 1u);
-      return seg * 512u + (uint32_t)rl * 16u;
-    };
-    auto wok = [&](int k0, bool (&ok)[RF]) {
-#pragma unroll
-      for (int f = 0; f < RF; ++f) ok[f] = fval[f] && (k0 + KQ * q < K);
-      return k0 + KQ * q + KQ <= K;
-    };
 
     // One K loop + epilogue per path: full token tiles run without any
     // per-fragment test, partial tiles skip the empty fragments.  The
@@ -656,34 +708,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   #pragma unroll
           for (int i = 0; i < MF::NC; ++i) acc[f][t][i] = 0.f;
 
-      auto load_w = [&](WChunk<RF, KQ> &w, int k0) {
-        if constexpr (TILED) {
-          load_wchunk_tiled(w, vr, mr, sr, fv, fm, fs, tlo(k0));
-        } else {
-          bool ok[RF];
-          const bool whole = wok(k0, ok);
-          uint32_t kv, km, ks;
-          koff(k0, kv, km, ks);
-          load_wchunk(w, vb, mb, sb, fv, fm, fs, vo, mo, so, ok, whole, kv, km, ks);
-        }
-      };
       if constexpr (RING) {
-        auto ring_load = [&](int slot, int k0) {
-          const uint32_t lo = tlo(k0);
-          uint8_t *base = wring + slot * RSLOT + wave * (RF * RFB);
-#pragma unroll
-          for (int f = 0; f < RF; ++f) {
-            uint8_t *fb = base + f * RFB;
-            buffer_to_lds<16>(vr, fb, lo, fv[f]);
-            if constexpr (PAIRED) {
-              buffer_to_lds<4>(mr, fb + RV, lo >> 2, fm[f]);
-            } else {
-              buffer_to_lds<4>(mr, fb + RV, lo >> 1, fm[f]);
-              buffer_to_lds<4>(mr, fb + RV + 256, (lo >> 1) + 4, fm[f]);
-            }
-            buffer_to_lds<2>(sr, fb + RV + RM, lo >> 3, fs[f]);
-          }
-        };
         // The ring is read with one asm block per fragment that waits for its
         // own reads (lgkmcnt): the waitcnt pass would otherwise make every
         // read of the ring wait for the slot still streaming in (vmcnt).
@@ -717,8 +742,6 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
             w.s[f] = sc;
           }
         };
-        ring_load(0, 0);
-        if (nk > 1) ring_load(1, KC);
         load_tok(tkA, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if constexpr (PAIRED) split_tok(tkA);
@@ -774,8 +797,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           }
         }
       } else if constexpr (PAIRED) {
-        PChunk<RF> wA, wB;
-        load_pchunk(wA, vr, mr, sr, fv, fm, fs, tlo(0));
+        PChunk<RF> wA = w0, wB;
         load_tok(tkA, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         split_tok(tkA);
@@ -804,8 +826,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           if (c + 1 < nk) chunk(c + 1, tkB, tkA, wB, wA);
         }
       } else {
-        WChunk<RF, KQ> wA, wB;
-        load_w(wA, 0);
+        WChunk<RF, KQ> wA = w0, wB;
         load_tok(tkA, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -899,32 +920,38 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
   auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
+  const size_t dyn = spgemm_sched_bytes(a.E);
   // upper bound of the item count: every expert may hold one partial tile
   const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
+  // workgroups per CU for this dynamic LDS size (cached per device and size)
   static thread_local int occ_dev = -1, occ = 1;
+  static thread_local size_t occ_dyn = 0;
   int dev = 0;
   (void)hipGetDevice(&dev);
-  if (occ_dev != dev) {
+  if (occ_dev != dev || occ_dyn != dyn) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, WAVES * 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, WAVES * 64, dyn) != hipSuccess ||
         o < 1)
       o = 1;
     occ = o;
     occ_dev = dev;
+    occ_dyn = dyn;
   }
   long long grid = (long long)device_cu_count() * occ;
   if (grid > items) grid = items;
   grid = (grid + 7) & ~7ll;          // XCD-major item spreading needs a multiple of 8
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), dyn, stream, a);
   return launch_status("moesq_grouped_spgemm");
 }
 
 // Tile choice.  Up to 32 routed rows per expert on average (a sweep over
 // active experts x rows per expert puts the crossover between 32 and 64
 // rows): the streaming tile, 16x16x32 MFMAs on 32 weight rows x 32 tokens
-// per wave, 256-position chunks, four waves per SIMD (two 8-wave workgroups
-// per CU).  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
+// per wave, 256-position chunks, in 4-wave workgroups of 128 weight rows
+// (three per CU): small decode batches have few (expert, row tile) items,
+// and items half as large spread them more evenly over the CUs (30B-class
+// decode: -12 % against 8-wave workgroups).  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
 // x 128 tokens per wave, two waves per SIMD, so that every decoded weight
 // feeds 4 MFMAs of 32 tokens.  Fragments are whole: the 32-row tile needs
 // the output rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the
@@ -936,6 +963,9 @@ template <int FMT>
 static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
   const bool small = (long long)a.M <= 32ll * a.E || out_rows % 32 != 0;
+  if (small && (long long)a.M <= 16ll * a.E)
+    return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
+                  : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
   if (small)
     return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
                   : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);

@@ -387,10 +387,11 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
 
   __shared__ uint4 lut[PAIRED ? 1 : 256];   // 4:8 selector table (paired needs none)
-  // Item order: every expert's whole token tiles first (expert order), then
-  // the partial tiles (at most one per expert) by descending fragment count.
-  // Workgroups take items in fixed rounds, so putting the costly items first
-  // and the cheap ones last balances the rounds (longest job first).
+  // Item order (contraction tiles): every expert's whole token tiles first
+  // (expert order), then the partial tiles (at most one per expert) by
+  // descending fragment count.  Workgroups take items in fixed rounds, so
+  // putting the costly items first and the cheap ones last balances the
+  // rounds (longest job first).  Streaming tiles: see STREAM below.
   // The three per-expert arrays sit in dynamic LDS sized for the launch's
   // E (spgemm_sched_bytes), so that a small expert count leaves room for
   // more workgroups per CU.
@@ -430,6 +431,13 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   auto off_at = [&](int e) { return min(max(a.offsets[e], 0), M); };
   for (int e = tid; e < E; e += WAVES * 64) s_cnt[e] = max(0, off_at(e + 1) - off_at(e));
   __syncthreads();
+  // Streaming tiles (16-row fragments) cost about the same whatever their
+  // row count (the weight decode dominates), so every token tile of an
+  // expert, partial or not, goes in the prefix in expert order, with the
+  // token tiles of one row tile next to each other: they read the same
+  // weights at the same time on one XCD, and the second read hits L2.
+  constexpr bool STREAM = MS == 16;
+  auto tiles_of = [&](int e) { return STREAM ? (s_cnt[e] + BM - 1) / BM : s_cnt[e] / BM; };
   if (wave == 0) {
     // by one wave: prefix of the whole tiles, then the partial tiles bucketed
     // by fragment count (TF down to 1), experts ascending within a bucket
@@ -444,16 +452,16 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       return v;
     };
     int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += s_cnt[e] / BM;
+    for (int e = e0; e < e1; ++e) sum += tiles_of(e);
     const int incl = scan(sum);
     int run = incl - sum;
     for (int e = e0; e < e1; ++e) {
       s_full[e] = run * a.row_tiles;
-      run += s_cnt[e] / BM;
+      run += tiles_of(e);
     }
     if (lane == 63) s_full[E] = incl * a.row_tiles;
     int base = 0;
-    for (int c = TF; c >= 1; --c) {
+    for (int c = STREAM ? 0 : TF; c >= 1; --c) {
       auto cls = [&](int e) {
         const int rem = s_cnt[e] % BM;
         return rem > 0 && (rem + MS - 1) / MS == c;
@@ -506,8 +514,14 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       }
       e = lo;
       const int local = item - s_full[e];
-      tt = local / a.row_tiles;
-      rt = local - tt * a.row_tiles;
+      if constexpr (STREAM) {
+        const int ntt = tiles_of(e);
+        rt = local / ntt;
+        tt = local - rt * ntt;
+      } else {
+        tt = local / a.row_tiles;
+        rt = local - tt * a.row_tiles;
+      }
     } else {
       const int j = (item - nfull) / a.row_tiles;
       rt = item - nfull - j * a.row_tiles;
@@ -947,11 +961,14 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 
 // Tile choice.  Up to 32 routed rows per expert on average (a sweep over
 // active experts x rows per expert puts the crossover between 32 and 64
-// rows): the streaming tile, 16x16x32 MFMAs on 32 weight rows x 32 tokens
-// per wave, 256-position chunks, in 4-wave workgroups of 128 weight rows
-// (three per CU): small decode batches have few (expert, row tile) items,
-// and items half as large spread them more evenly over the CUs (30B-class
-// decode: -12 % against 8-wave workgroups).  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
+// rows): the streaming tile, 16x16x32 MFMAs on 32 weight rows per wave,
+// 256-position chunks.  Up to 4 rows per expert on average it runs one
+// 16-token fragment in 4-wave workgroups of 128 weight rows (four per CU):
+// decode batches have few (expert, row tile) items, and items half as large
+// spread them more evenly over the CUs (30B-class decode -17 %); an expert
+// with more rows takes several token tiles, each decoding the weights again,
+// so above that average the 8-wave tile with two fragments (32 tokens)
+// runs.  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
 // x 128 tokens per wave, two waves per SIMD, so that every decoded weight
 // feeds 4 MFMAs of 32 tokens.  Fragments are whole: the 32-row tile needs
 // the output rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the
@@ -963,7 +980,7 @@ template <int FMT>
 static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
   const bool small = (long long)a.M <= 32ll * a.E || out_rows % 32 != 0;
-  if (small && (long long)a.M <= 16ll * a.E)
+  if (small && (long long)a.M <= 4ll * a.E)
     return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
                   : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
   if (small)

@@ -166,10 +166,11 @@ def _paired_case(lib, loads, N, K, swiglu, seed):
     ([40] * 4, 64, 64, False),                             # K below one chunk
     ([300, 260], 576, 512, True),                          # 32-row tile, SwiGLU
     ([0, 3, 0, 1], 32, 64, False),
-    # tile choice boundaries (E = 4): one-fragment streaming tile at M = 16E,
-    # two-fragment streaming tile at 16E + 1 and 32E, contraction at 32E + 1
-    ([40, 0, 20, 4], 64, 512, True),
-    ([40, 1, 20, 4], 64, 512, False),
+    # tile choice boundaries: one-fragment streaming tile at M = 4E (an
+    # expert of 20 rows takes two token tiles), two-fragment streaming tile
+    # at 4E + 1 and 32E, contraction at 32E + 1
+    ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, True),
+    ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, False),
     ([80, 0, 40, 8], 128, 512, True),
     ([80, 1, 40, 8], 128, 512, False),
     # the largest expert count: 1024 experts of 0-2 rows

@@ -304,11 +304,11 @@ def test_spgemm_edges(lib, loads, N, K, swiglu):
     ([5, 0, 64, 127, 128, 129, 1], 32, 448, False),
     ([1] * 20, 128, 256, True),
     ([40] * 4, 64, 64, False),
-    # tile choice boundaries (E = 4): M = 16E one-fragment streaming tile
-    # (an expert of 40 rows takes three token tiles), 16E + 1 and 32E the
-    # two-fragment streaming tile, 32E + 1 the contraction tile
-    ([40, 0, 20, 4], 64, 512, False),
-    ([40, 1, 20, 4], 64, 512, True),
+    # tile choice boundaries: M = 4E one-fragment streaming tile (an expert
+    # of 20 rows takes two token tiles), 4E + 1 and 32E the two-fragment
+    # streaming tile, 32E + 1 the contraction tile
+    ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, False),
+    ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, True),
     ([80, 0, 40, 8], 128, 512, False),
     ([80, 1, 40, 8], 128, 512, True),
     # the largest expert count: 1024 experts of 0-2 rows

@@ -26,7 +26,7 @@ workload.  Decode lines also carry the rate of a plain streaming read of
 4 GiB on the same device (`read_ceiling_gbs`), the practical bound of a
 weight stream.
 
---paired runs the same step on paired 4:8 weights (two of the four adjacent
+--paired runs the same step on paired 4:8 weights (two of the four position
 pairs of a group kept, 2.75 bits per weight) through the sparse MFMA.
 """
 from __future__ import annotations

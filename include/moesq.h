@@ -17,8 +17,8 @@
  *   unpermute  combine: back to token order, optionally         ("D.1", "D.3 End-to-end serving
  *              weighted by the router                            benchmark")
  *   pack_weights  compress dense fp32 experts into the format   ("3.4 Implementation details":
- *                                                               E2M1 values, sparse metadata and
- *                                                               one scale per 32 logical weights)
+ *                                                               FP4 codes, sparsity metadata,
+ *                                                               a scale for each 32 weights)
  *
  * Conventions (every call):
  *   - Pointers are DEVICE pointers unless marked "host".  bf16 tensors are
@@ -120,9 +120,9 @@ typedef struct {
 /*
  * MOESQ_LAYOUT_PAIRED: the pages' paired 4:8 format ("A Sparse-quantized
  * representation": each group of eight keeps two of its four adjacent pairs,
- * six patterns; "Storage layout": four kept values and a pattern index per
- * group plus a UE4M3 scale per 32 weights, 2.75 bits per weight).  The
- * `masks` pointer carries the pattern indices:
+ * six patterns; "Storage layout": per group its four kept FP4 codes and
+ * the index of its pattern, per 32 weights one unsigned E4M3 scale, 2.75
+ * bits per weight).  The `masks` pointer carries the pattern indices:
  *
  *   values [E][N][K/4]   as the canonical layout (four kept codes per group,
  *                        ascending position, lower one in the low nibble)
@@ -236,8 +236,9 @@ moesq_status_t moesq_unpermute(const uint16_t *y, const int32_t *inv_perm,
 
 /*
  * Compress dense fp32 experts into the canonical layout above
- * ("3.4 Implementation details": scales recomputed, then E2M1 values, sparse
- * metadata and a scale per 32 logical weights packed).  Per expert:
+ * ("3.4 Implementation details": the scales are recomputed first, then the
+ * FP4 codes, the sparsity masks and one scale per 32 weights are stored).
+ * Per expert:
  *   support  keep the 4 largest |w| of every group of 8; equal |w| -> lower position
  *   g        = amax / 2688 in fp32 (2688 = 6*448), g = 1 if amax == 0
  *   s_b      = E4M3 round-to-nearest-even, saturating at 448, of amax_b / (6*g)

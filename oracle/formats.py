@@ -1,10 +1,10 @@
 """Value codes: E2M1 (FP4), E4M3 (FP8) and bf16 rounding.  ORACLE (test
 infrastructure only).
 
-The pages name the formats only ("retained values use the E2M1 grid", "one
-UE4M3 scale per 32 logical weights": paper summary page, "A Sparse-quantized
-representation", Blackwell paired 4:8 NVFP4 / Storage layout) and cite the
-OCP Microscaling formats paper for them.  The definitions used here are the
+The pages only name the formats (kept values on the FP4 E2M1 grid, one
+unsigned E4M3 scale per 32 logical weights: paper summary page, "A
+Sparse-quantized representation", Blackwell paired 4:8 NVFP4 / Storage
+layout) and cite the OCP Microscaling formats paper for them.  The definitions used here are the
 standard ones of those formats:
 
   E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, no inf/NaN.

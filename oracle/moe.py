@@ -6,8 +6,9 @@ Paper summary page:
     problems in one launch, expert weights as the sparse operand.
   * "D.1 Implementation details": dispatch feeds the first expert GEMM,
     SwiGLU output preparation feeds the second, then scatter/combine.
-  * "D.3 End-to-end serving benchmark": token combination and output layout
-    are fixed outside the expert kernel.
+  * "D.3 End-to-end serving benchmark": how tokens are combined and how the
+    output is laid out is decided outside the expert kernel and kept the
+    same for every backend.
 
 Y[r, :] = X_routed[r, :] @ W_e^T for the expert e owning routed row r; the
 inputs are the bf16 tokens (exact in float64) and the exactly decoded expert

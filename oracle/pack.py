@@ -1,9 +1,9 @@
 """Compression of one dense expert matrix to the 4:8 / E2M1 / E4M3 format and
 its exact decode.  ORACLE (test infrastructure only).
 
-Follows the paper summary page, "3.4 Implementation details" (scales are
-recomputed, then E2M1 values, sparse metadata and a scale per 32 logical
-weights are packed) and "A Sparse-quantized representation" (each group of
+Follows the paper summary page, "3.4 Implementation details" (after the
+scales are recomputed the packer stores the FP4 codes, the sparsity metadata
+and one scale for each 32 logical weights) and "A Sparse-quantized representation" (each group of
 eight keeps four values; 16 kept values of a 32-weight block share one scale;
 zero lies on the grid so pruned positions are feasible).  The selection of
 the support here is the hard top-4 by magnitude; the pages learn it, which is

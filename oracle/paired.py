@@ -2,12 +2,13 @@
 format and its exact decode.  ORACLE (test infrastructure only).
 
 Follows the paper summary page, "A Sparse-quantized representation":
-  * Blackwell paired 4:8 NVFP4 -- a group of eight weights keeps two of its
-    four adjacent pairs (positions 2i, 2i+1), so six patterns are allowed;
+  * Blackwell paired 4:8 NVFP4 -- of the four position pairs (2i, 2i+1) of
+    a group of eight weights, two are kept, so six patterns are allowed;
     the 16 kept values of a 32-weight block share one UE4M3 scale and the
     kept values lie on the E2M1 grid.
-  * Storage layout -- per group of eight, four kept values and a pattern
-    index; per 32-weight block, one UE4M3 scale: 2.75 bits per weight.
+  * Storage layout -- a group of eight stores its four kept codes and the
+    number of its pattern, a 32-weight block one UE4M3 scale: 2.75 bits per
+    weight.
 
 Readings where the pages are silent:
   * pattern index: p in [0, 6) numbers the kept pair couples (i, j), i < j,

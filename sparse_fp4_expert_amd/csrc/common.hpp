@@ -105,7 +105,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// ---- paired 4:8 ("Blackwell paired 4:8 NVFP4": two of the four adjacent
+// ---- paired 4:8 ("Blackwell paired 4:8 NVFP4": two of the four position
 // pairs of a group of eight are kept, six patterns).
 //
 // Reordering a group's positions as (0,2,4,6 | 1,3,5,7) turns every paired

@@ -1,9 +1,9 @@
 // Compression of dense fp32 experts into the 4:8 / E2M1 / E4M3 layout, and a
 // decode-to-dense kernel that exercises the GEMM's in-register decoder.
 //
-// Paper summary page, "3.4 Implementation details": scales are recomputed,
-// then E2M1 values, sparse metadata and a UE4M3 scale per 32 logical weights
-// are packed.  "A Sparse-quantized representation": 4 of every 8 weights are
+// Paper summary page, "3.4 Implementation details": after the scales are
+// recomputed, the packer stores the FP4 (E2M1) codes, the sparsity metadata
+// and one unsigned E4M3 scale for every block of 32 logical weights.  "A Sparse-quantized representation": 4 of every 8 weights are
 // kept, the 16 kept values of a 32-weight block share the scale, and zero is
 // on the grid.  The support here is the hard top-4 by magnitude.
 //
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(PACK_THREADS) void decode_kernel(
   dense[G] = decode_group<0>(masks[mo], v, s, lut);
 }
 
-// ---- paired 4:8 ("Blackwell paired 4:8 NVFP4": two of the four adjacent
+// ---- paired 4:8 ("Blackwell paired 4:8 NVFP4": two of the four position
 // pairs (2i, 2i+1) of a group are kept).  The pair sums decide in fp32; pair
 // i is kept iff fewer than two pairs beat it (a larger sum, or an equal sum
 // at a lower index), which always keeps exactly two.  Returns the keep-mask

@@ -682,10 +682,55 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     // slot P = L % UPR holds logical unit-half h = (P ^ row) & 1, the same
     // for every 1 KB block of the lane, since a block starts at an even row
     // and covers 64 / UPR rows.  Both slots are read before either is
-    // written: LDS instructions of one wave run in order.
+    // written: LDS instructions of one wave run in order.  The batched path
+    // (four blocks per wave) leaves its writes in flight: every caller waits
+    // (lgkmcnt(0), in asm,
+    // which the compiler cannot drop as it can a fence's wait for LDS work it
+    // does not know of) before its barrier.
     const int split_h = ((lane % UPR) ^ (lane / UPR)) & 1;
     const uint32_t split_sel = split_h ? 0x07060302u : 0x05040100u;
     auto split_tok = [&](uint16_t *buf) {
+      if constexpr (BPW == 4) {
+        if ((wave * BPW + BPW - 1) * (64 / UPR) < nrows) {
+          // all four blocks loaded: every read first (one wait), then the
+          // perms, then every write (block j sits 1 KB after block j-1); the
+          // caller waits for the writes before its barrier.  One wait per
+          // chunk instead of two per block: paired prefill-1t -1.4 % (gate/up)
+          // and -2 % (down), prefill-30b -5 %.
+          const uint32_t blk = lds_addr(buf + (wave * BPW) * 512);
+          const uint32_t a_own = blk + 16u * lane, a_nbr = blk + 16u * (lane ^ 1);
+          u32x4_t x0, y0, x1, y1, x2, y2, x3, y3;
+          asm volatile(
+              "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
+              "ds_read_b128 %2, %8 offset:1024\n\tds_read_b128 %3, %9 offset:1024\n\t"
+              "ds_read_b128 %4, %8 offset:2048\n\tds_read_b128 %5, %9 offset:2048\n\t"
+              "ds_read_b128 %6, %8 offset:3072\n\tds_read_b128 %7, %9 offset:3072\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(x0), "=&v"(y0), "=&v"(x1), "=&v"(y1), "=&v"(x2), "=&v"(y2), "=&v"(x3),
+                "=&v"(y3)
+              : "v"(a_own), "v"(a_nbr)
+              : "memory");
+          auto pk = [&](const u32x4_t &v) {
+            u32x2_t r;
+            r[0] = __builtin_amdgcn_perm(v[1], v[0], split_sel);
+            r[1] = __builtin_amdgcn_perm(v[3], v[2], split_sel);
+            return r;
+          };
+          const u32x2_t o0 = pk(x0), n0 = pk(y0), o1 = pk(x1), n1 = pk(y1), o2 = pk(x2),
+                        n2 = pk(y2), o3 = pk(x3), n3 = pk(y3);
+          const uint32_t w_own = a_own + 8u * split_h, w_nbr = a_own + 8u * (split_h ^ 1);
+          asm volatile(
+              "ds_write_b64 %0, %2\n\tds_write_b64 %1, %3\n\t"
+              "ds_write_b64 %0, %4 offset:1024\n\tds_write_b64 %1, %5 offset:1024\n\t"
+              "ds_write_b64 %0, %6 offset:2048\n\tds_write_b64 %1, %7 offset:2048\n\t"
+              "ds_write_b64 %0, %8 offset:3072\n\tds_write_b64 %1, %9 offset:3072"
+              :
+              : "v"(w_own), "v"(w_nbr), "v"(o0), "v"(n0), "v"(o1), "v"(n1), "v"(o2), "v"(n2),
+                "v"(o3), "v"(n3)
+              : "memory");
+          return;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         if ((wave * BPW + j) * (64 / UPR) >= nrows) break;   // block never loaded
@@ -815,6 +860,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         load_tok(tkA, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         split_tok(tkA);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the split's writes
         __syncthreads();
         auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, PChunk<RF> &wc,
                          PChunk<RF> &wn) {
@@ -833,6 +879,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           mma_chunk_paired<MS, RF, TF, KC, FULL>(acc, cur, wc, nft, q, rl);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           if (c + 1 < nk) split_tok(nxt);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the split's writes
           __syncthreads();
         };
         for (int c = 0; c < nk; c += 2) {

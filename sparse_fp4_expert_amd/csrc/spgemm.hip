@@ -774,6 +774,30 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         const uint32_t ring0 = lds_addr(wring) + (uint32_t)(wave * (RF * RFB));
         using WC = std::conditional_t<PAIRED, PChunk<RF>, WChunk<RF, KQ>>;
         auto ring_read = [&](WC &w, int slot) {
+          if constexpr (PAIRED && RF == 2) {
+            // both fragments in one block with one wait (fragment 1 sits RFB
+            // bytes after fragment 0)
+            const uint32_t fb = ring0 + (uint32_t)(slot * RSLOT);
+            const uint32_t av = fb + lane * 16, am = fb + RV + lane * 4, as = fb + RV + RM + lane * 4;
+            u32x4_t v0, v1;
+            uint32_t m0, m1, s0, s1;
+            asm volatile("ds_read_b128 %0, %6\n\tds_read_b32 %1, %7\n\tds_read_u16 %2, %8\n\t"
+                         "ds_read_b128 %3, %6 offset:%9\n\tds_read_b32 %4, %7 offset:%9\n\t"
+                         "ds_read_u16 %5, %8 offset:%9\n\ts_waitcnt lgkmcnt(0)"
+                         : "=&v"(v0), "=&v"(m0), "=&v"(s0), "=&v"(v1), "=&v"(m1), "=&v"(s1)
+                         : "v"(av), "v"(am), "v"(as), "n"(RFB)
+                         : "memory");
+            w.w[0] = m0;
+            w.w[1] = m1;
+            w.s[0] = s0;
+            w.s[1] = s1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              w.v[0][i] = v0[i];
+              w.v[1][i] = v1[i];
+            }
+            return;
+          }
 #pragma unroll
           for (int f = 0; f < RF; ++f) {
             const uint32_t fb = ring0 + (uint32_t)(slot * RSLOT + f * RFB);

@@ -315,16 +315,24 @@ __device__ __forceinline__ void mma_chunk_paired(typename Smfmac<MS>::C (&acc)[R
     return __builtin_bit_cast(bf16x16_t, lh);
   };
   dec(A[0], I[0], 0);
+  // token fragments one ahead: two B operands (16 VGPRs) live, not TF.  The
+  // 32-row tile also carries the lookahead across steps (the last fragment
+  // of step s loads the first of step s+1); on the 16-row tile that costs
+  // spills.
+  constexpr bool ACROSS = MS == 32;
+  bf16x16_t B = load_b(0, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    // token fragments one ahead: two B operands (16 VGPRs) live, not TF
-    bf16x16_t B = load_b(0, s);
+    if (!ACROSS && s > 0) B = load_b(0, s);
     if (s + 1 < 4) dec(A[(s + 1) & 1], I[(s + 1) & 1], s + 1);
 #pragma unroll
     for (int t = 0; t < TF; ++t) {
       if (!FULL && t >= nft) break;
       bf16x16_t Bn = B;
-      if (t + 1 < TF && (FULL || t + 1 < nft)) Bn = load_b(t + 1, s);
+      if (t + 1 < TF && (FULL || t + 1 < nft))
+        Bn = load_b(t + 1, s);
+      else if (ACROSS && s + 1 < 4)
+        Bn = load_b(0, s + 1);
 #pragma unroll
       for (int f = 0; f < RF; ++f)
         acc[f][t] = Smfmac<MS>::run(A[s & 1][f], B, acc[f][t], I[s & 1][f]);

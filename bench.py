@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of steps: time the first grouped GEMM of --workload over a grid "
                          "of active-expert counts G x rows per expert R (one JSON line per point)")
+    ap.add_argument("--sweep-experts", default="1,4,16,64,128,384",
+                    help="comma-separated active-expert counts G of --sweep")
+    ap.add_argument("--sweep-rows", default="1,2,4,8,16,32,64",
+                    help="comma-separated rows per expert R of --sweep")
     ap.add_argument("--paired", action="store_true",
                     help="paired 4:8 weights (2.75 bits per weight) on the sparse MFMA instead of "
                          "the unconstrained 4:8 format")
@@ -431,7 +435,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     if args.sweep:
-        sweep(m, wl, paired=args.paired)
+        sweep(m, wl, Gs=tuple(int(v) for v in args.sweep_experts.split(",")),
+              Rs=tuple(int(v) for v in args.sweep_rows.split(",")), paired=args.paired)
         return
     step = Step(m, wl, fused=not args.unfused, paired=args.paired)
     torch.cuda.synchronize()
@@ -467,13 +472,15 @@ def main():
     if prefill:
         roof = {"bound": "mfma", "achieved": f0 / (g0_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
-        # MFMAs the kernel executes: each expert's rows padded to whole
-        # 32-row token fragments (the prefill tile); one MAC per kept weight
-        # is the useful rate.  Paired weights run on the sparse MFMA, whose
-        # pipe retires twice the dense-equivalent work of the dense MFMA.
+        # MFMAs the kernels execute: each expert's rows padded to whole token
+        # fragments, 32 rows on the contraction tile (experts of more than 32
+        # rows), 16 on the streaming tile (the others); one MAC per kept
+        # weight is the useful rate.  Paired weights run on the sparse MFMA,
+        # whose pipe retires twice the dense-equivalent work of the dense MFMA.
         _, N0, K0 = wl.proj[0]
         counts = np.bincount(step.ids_host, minlength=wl.E)
-        padded = float((-(-counts // 32) * 32).sum())
+        big = counts > 32
+        padded = float((-(-counts[big] // 32) * 32).sum() + (-(-counts[~big] // 16) * 16).sum())
         pipe_peak = PEAK_BF16_TFLOPS * (2 if args.paired else 1)
         roof["mfma_executed_tflops"] = 2.0 * padded * N0 * K0 / (g0_ms * 1e-3) / 1e12
         roof["mfma_executed_frac"] = roof["mfma_executed_tflops"] / pipe_peak

@@ -2,7 +2,9 @@
 //
 // Paper summary page, "3.4 Implementation details": grouped execution runs
 // every routing-dependent expert problem within one launch, with the sparse
-// weights as the first MMA operand.  Here the weights stay compressed in HBM
+// weights as the first MMA operand (here: one launch per tiling, each over
+// the experts of its size range; see the tile choice at the end).  The
+// weights stay compressed in HBM
 // (13/32 byte per logical weight) and are decoded in registers straight into
 // the A operand of a bf16 MFMA (v_mfma_f32_16x16x32_bf16 or
 // v_mfma_f32_32x32x16_bf16): the decoded values E2M1*E4M3 are exact in bf16,
@@ -27,6 +29,7 @@
 // group per lane -- while the B fragment holds the same 8 positions of the
 // lane's token.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "common.hpp"
@@ -45,6 +48,7 @@ struct SpgemmArgs {
   uint16_t *y;
   int M, E, N, K;
   int row_tiles;
+  int rows_lo, rows_hi;     // this launch takes the experts with rows_lo < rows <= rows_hi
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -437,7 +441,12 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   // expert row ranges straight from the offsets (clamped to [0, M]); only
   // the item prefix is kept in LDS
   auto off_at = [&](int e) { return min(max(a.offsets[e], 0), M); };
-  for (int e = tid; e < E; e += WAVES * 64) s_cnt[e] = max(0, off_at(e + 1) - off_at(e));
+  // routed rows per expert; experts outside this launch's row range count as
+  // empty (another launch of the same call takes them)
+  for (int e = tid; e < E; e += WAVES * 64) {
+    const int c = max(0, off_at(e + 1) - off_at(e));
+    s_cnt[e] = (c > a.rows_lo && c <= a.rows_hi) ? c : 0;
+  }
   __syncthreads();
   // Streaming tiles (16-row fragments) cost about the same whatever their
   // row count (the weight decode dominates), so every token tile of an
@@ -1038,33 +1047,48 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   return launch_status("moesq_grouped_spgemm");
 }
 
-// Tile choice.  Up to 32 routed rows per expert on average (a sweep over
-// active experts x rows per expert puts the crossover between 32 and 64
-// rows): the streaming tile, 16x16x32 MFMAs on 32 weight rows per wave,
-// 256-position chunks.  Up to 4 rows per expert on average it runs one
-// 16-token fragment in 4-wave workgroups of 128 weight rows (four per CU):
-// decode batches have few (expert, row tile) items, and items half as large
-// spread them more evenly over the CUs (30B-class decode -17 %); an expert
-// with more rows takes several token tiles, each decoding the weights again,
-// so above that average the 8-wave tile with two fragments (32 tokens)
-// runs.  Otherwise the contraction tile, 32x32x16 MFMAs on 64 weight rows
-// x 128 tokens per wave, two waves per SIMD, so that every decoded weight
-// feeds 4 MFMAs of 32 tokens.  Fragments are whole: the 32-row tile needs
-// the output rows (N, or N/2 under SwiGLU) to be a multiple of 32, else the
-// 16-row tile runs.
-// Paired weights take the same two tiles on the sparse MFMA
-// (16x16x64 and 32x32x32): the same token and weight-row counts per wave,
-// each step contracting twice the dense K.
+// Tile choice.  The streaming tile: 16x16x32 MFMAs on 32 weight rows per
+// wave, 256-position chunks.  The contraction tile: 32x32x16 MFMAs on 64
+// weight rows x 128 tokens per wave, two waves per SIMD, so that every
+// decoded weight feeds 4 MFMAs of 32 tokens.  A sweep over active experts x
+// rows per expert puts their crossover between 32 and 64 rows per expert.
+// Up to 4 rows per expert on average (decode batches) one launch runs the
+// streaming tile with one 16-token fragment in 4-wave workgroups of 128
+// weight rows (four per CU): such batches have few (expert, row tile)
+// items, and items half as large spread them more evenly over the CUs
+// (30B-class decode -17 %); an expert with more rows takes several token
+// tiles.  Otherwise two launches split the experts by their own row counts,
+// which only the device knows: experts of up to 32 rows on the 8-wave
+// streaming tile with two fragments (32 tokens), larger ones on the
+// contraction tile (trillion-class prefill: gate/up -1 to -3 % on 4:8
+// weights, -8 % on paired ones, whose contraction tile runs partial token
+// tiles as full).  Fragments are whole: the 32-row tile needs the output
+// rows (N, or N/2 under SwiGLU) to be a multiple of 32, else one launch of
+// the streaming tile takes every expert.
+// Paired weights take the same tiles on the sparse MFMA (16x16x64 and
+// 32x32x32): the same token and weight-row counts per wave, each step
+// contracting twice the dense K.
 template <int FMT>
-static moesq_status_t launch_layout(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
+static moesq_status_t launch_layout(SpgemmArgs a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
-  const bool small = (long long)a.M <= 32ll * a.E || out_rows % 32 != 0;
-  if (small && (long long)a.M <= 4ll * a.E)
+  a.rows_lo = 0;
+  a.rows_hi = INT_MAX;
+  // decode batches: one launch of the one-fragment streaming tile
+  if ((long long)a.M <= 4ll * a.E)
     return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
                   : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
-  if (small)
+  if (out_rows % 32 != 0)   // the 32-row tile needs whole 32-row fragments
     return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
                   : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  // otherwise two launches, split by each expert's own row count (read on
+  // the device): up to 32 rows the two-fragment streaming tile, above it
+  // the contraction tile
+  a.rows_hi = 32;
+  moesq_status_t st = swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
+                             : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  if (st != MOESQ_OK) return st;
+  a.rows_lo = 32;
+  a.rows_hi = INT_MAX;
   return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
                 : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
 }

@@ -166,9 +166,10 @@ def _paired_case(lib, loads, N, K, swiglu, seed):
     ([40] * 4, 64, 64, False),                             # K below one chunk
     ([300, 260], 576, 512, True),                          # 32-row tile, SwiGLU
     ([0, 3, 0, 1], 32, 64, False),
-    # tile choice boundaries: one-fragment streaming tile at M = 4E (an
-    # expert of 20 rows takes two token tiles), two-fragment streaming tile
-    # at 4E + 1 and 32E, contraction at 32E + 1
+    # tile choice: M = 4E one launch of the one-fragment streaming tile (an
+    # expert of 20 rows takes two token tiles); above, experts of up to 32
+    # rows on the two-fragment streaming tile and larger ones on the
+    # contraction tile, in two launches
     ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, True),
     ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, False),
     ([80, 0, 40, 8], 128, 512, True),

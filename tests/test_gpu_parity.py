@@ -304,9 +304,10 @@ def test_spgemm_edges(lib, loads, N, K, swiglu):
     ([5, 0, 64, 127, 128, 129, 1], 32, 448, False),
     ([1] * 20, 128, 256, True),
     ([40] * 4, 64, 64, False),
-    # tile choice boundaries: M = 4E one-fragment streaming tile (an expert
-    # of 20 rows takes two token tiles), 4E + 1 and 32E the two-fragment
-    # streaming tile, 32E + 1 the contraction tile
+    # tile choice: M = 4E one launch of the one-fragment streaming tile (an
+    # expert of 20 rows takes two token tiles); above, experts of up to 32
+    # rows on the two-fragment streaming tile and larger ones on the
+    # contraction tile, in two launches
     ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, False),
     ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, True),
     ([80, 0, 40, 8], 128, 512, False),

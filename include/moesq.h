@@ -179,9 +179,9 @@ moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, 
                              int32_t K, uint16_t *x_routed, hipStream_t stream);
 
 /*
- * Grouped sparse GEMM over all experts in one call (one kernel launch for
- * decode-sized batches, else two: experts of up to 32 rows and larger ones
- * on different tilings, split on the device):
+ * Grouped sparse GEMM over all experts in one call (one kernel launch, or
+ * for large calls two: experts of up to 32 rows and larger ones on
+ * different tilings, split on the device):
  *   for every expert e and routed row r in [offsets[e], offsets[e+1]):
  *     acc[r][n] = sum_k x_routed[r][k] * W~_e[n][k]   (fp32 accumulation, the
  *                 decoded bf16 weights W~ = E2M1*E4M3 are exact)

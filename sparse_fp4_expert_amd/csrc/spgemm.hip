@@ -1057,12 +1057,15 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // weight rows (four per CU): such batches have few (expert, row tile)
 // items, and items half as large spread them more evenly over the CUs
 // (30B-class decode -17 %); an expert with more rows takes several token
-// tiles.  Otherwise two launches split the experts by their own row counts,
-// which only the device knows: experts of up to 32 rows on the 8-wave
-// streaming tile with two fragments (32 tokens), larger ones on the
-// contraction tile (trillion-class prefill: gate/up -1 to -3 % on 4:8
-// weights, -8 % on paired ones, whose contraction tile runs partial token
-// tiles as full).  Fragments are whole: the 32-row tile needs the output
+// tiles.  Larger GEMMs (at least ~5e11 multiply-adds) make two launches
+// that split the experts by their own row counts, which only the device
+// knows: experts of up to 32 rows on the 8-wave streaming tile with two
+// fragments (32 tokens), larger ones on the contraction tile
+// (trillion-class prefill: gate/up -1 to -3 % on 4:8 weights, -8 % on
+// paired ones, whose contraction tile runs partial token tiles as full).
+// Shorter ones (30B-class prefill, 1e11) lose more to the second launch
+// than they gain (+5 to 8 %) and make one launch, the streaming tile up to
+// 32 rows per expert on average, else the contraction tile.  Fragments are whole: the 32-row tile needs the output
 // rows (N, or N/2 under SwiGLU) to be a multiple of 32, else one launch of
 // the streaming tile takes every expert.
 // Paired weights take the same tiles on the sparse MFMA (16x16x64 and
@@ -1080,6 +1083,15 @@ static moesq_status_t launch_layout(SpgemmArgs a, bool swiglu, hipStream_t strea
   if (out_rows % 32 != 0)   // the 32-row tile needs whole 32-row fragments
     return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
                   : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  // A GEMM under ~5e11 multiply-adds is too short to pay for a second
+  // launch: one launch, its tile from the average rows per expert.
+  if ((double)a.M * a.N * a.K < 5.5e11) {
+    if ((long long)a.M <= 32ll * a.E)
+      return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
+                    : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+    return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
+                  : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
+  }
   // otherwise two launches, split by each expert's own row count (read on
   // the device): up to 32 rows the two-fragment streaming tile, above it
   // the contraction tile

@@ -774,13 +774,14 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     // One K loop + epilogue per path: full token tiles run without any
     // per-fragment test, partial tiles skip the empty fragments.  The
     // accumulators live inside each path, so they are never merged.
-    auto run_item = [&](auto full_tag) {
+    auto run_item = [&](auto full_tag, auto nf_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
-      typename MF::C acc[RF][TF];
+      constexpr int NF = decltype(nf_tag)::value;   // token fragments computed
+      typename MF::C acc[RF][NF];
   #pragma unroll
       for (int f = 0; f < RF; ++f)
   #pragma unroll
-        for (int t = 0; t < TF; ++t)
+        for (int t = 0; t < NF; ++t)
   #pragma unroll
           for (int i = 0; i < MF::NC; ++i) acc[f][t][i] = 0.f;
 
@@ -873,9 +874,9 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
             }
           }
           if constexpr (PAIRED)
-            mma_chunk_paired<MS, RF, TF, KC, FULL>(acc, cur, wc, nft, q, rl);
+            mma_chunk_paired<MS, RF, NF, KC, FULL>(acc, cur, wc, nft, q, rl);
           else
-            mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
+            mma_chunk<MS, RF, NF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
           if (c + 2 < nk)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING_LOADS) : "memory");
           else
@@ -917,7 +918,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
 #pragma unroll
               for (int i = 0; i < 4; ++i) wc.v[f][i] = ok ? wc.v[f][i] : 0u;
           }
-          mma_chunk_paired<MS, RF, TF, KC, FULL>(acc, cur, wc, nft, q, rl);
+          mma_chunk_paired<MS, RF, NF, KC, FULL>(acc, cur, wc, nft, q, rl);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           if (c + 1 < nk) split_tok(nxt);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the split's writes
@@ -951,7 +952,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
                 for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) wc.m[f][i] = ok ? wc.m[f][i] : 0u;
             }
           }
-          mma_chunk<MS, RF, TF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
+          mma_chunk<MS, RF, NF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
         };
@@ -967,7 +968,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       // fragment: four consecutive rows per group of four, one 8-byte store.
       const float g = a.gscale[e];
   #pragma unroll
-      for (int t = 0; t < TF; ++t) {
+      for (int t = 0; t < NF; ++t) {
         const int trow = t * MS + rl;
         if (trow >= ntok) continue;
         const size_t out_r = (size_t)(tok0 + trow);
@@ -1006,14 +1007,24 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         }
       }
     };
-    // The ring tile runs partial token tiles as full ones: fragments past
-    // the routed rows compute on stale LDS rows whose outputs are never
-    // stored, which keeps the accumulators free of branches (with them the
-    // tile spills).
-    if (RING || nft == TF)
-      run_item(std::true_type{});
-    else
-      run_item(std::false_type{});
+    // The ring tile takes partial token tiles on a K loop of their own per
+    // fragment count (per-fragment branches inside one loop made its
+    // accumulators spill); the other tiles test the fragments at run time.
+    using std::integral_constant;
+    if constexpr (RING) {
+      if (nft <= 1)
+        run_item(std::true_type{}, integral_constant<int, 1>{});
+      else if (nft == 2)
+        run_item(std::true_type{}, integral_constant<int, (TF < 2 ? TF : 2)>{});
+      else if (nft == 3)
+        run_item(std::true_type{}, integral_constant<int, (TF < 3 ? TF : 3)>{});
+      else
+        run_item(std::true_type{}, integral_constant<int, TF>{});
+    } else if (nft == TF) {
+      run_item(std::true_type{}, integral_constant<int, TF>{});
+    } else {
+      run_item(std::false_type{}, integral_constant<int, TF>{});
+    }
   }
 }
 
@@ -1062,7 +1073,7 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // knows: experts of up to 32 rows on the 8-wave streaming tile with two
 // fragments (32 tokens), larger ones on the contraction tile
 // (trillion-class prefill: gate/up -1 to -3 % on 4:8 weights, -8 % on
-// paired ones, whose contraction tile runs partial token tiles as full).
+// paired ones).
 // Shorter ones (30B-class prefill, 1e11) lose more to the second launch
 // than they gain (+5 to 8 %) and make one launch, the streaming tile up to
 // 32 rows per expert on average, else the contraction tile.  Fragments are whole: the 32-row tile needs the output

@@ -1007,11 +1007,12 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         }
       }
     };
-    // The ring tile takes partial token tiles on a K loop of their own per
-    // fragment count (per-fragment branches inside one loop made its
-    // accumulators spill); the other tiles test the fragments at run time.
+    // The contraction tiles take partial token tiles on a K loop of their
+    // own per fragment count (per-fragment branches inside one loop made
+    // the ring tile's accumulators spill, and cost the 4:8 tile 1-3 %); the
+    // streaming tiles test the fragments at run time.
     using std::integral_constant;
-    if constexpr (RING) {
+    if constexpr (RING || MS == 32) {
       if (nft <= 1)
         run_item(std::true_type{}, integral_constant<int, 1>{});
       else if (nft == 2)

@@ -180,7 +180,7 @@ moesq_status_t moesq_permute(const uint16_t *x, const int32_t *perm, int32_t T, 
 
 /*
  * Grouped sparse GEMM over all experts in one call (one kernel launch, or
- * for large calls two: experts of up to 32 rows and larger ones on
+ * for large calls three: experts of up to 16, up to 32 and more rows on
  * different tilings, split on the device):
  *   for every expert e and routed row r in [offsets[e], offsets[e+1]):
  *     acc[r][n] = sum_k x_routed[r][k] * W~_e[n][k]   (fp32 accumulation, the

@@ -1069,10 +1069,11 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // weight rows (four per CU): such batches have few (expert, row tile)
 // items, and items half as large spread them more evenly over the CUs
 // (30B-class decode -17 %); an expert with more rows takes several token
-// tiles.  Larger GEMMs (at least ~5e11 multiply-adds) make two launches
+// tiles.  Larger GEMMs (at least ~5e11 multiply-adds) make three launches
 // that split the experts by their own row counts, which only the device
-// knows: experts of up to 32 rows on the 8-wave streaming tile with two
-// fragments (32 tokens), larger ones on the contraction tile
+// knows: experts of up to 16 rows on the one-fragment streaming tile, up
+// to 32 on the 8-wave streaming tile with two fragments (32 tokens), larger
+// ones on the contraction tile
 // (trillion-class prefill: gate/up -1 to -3 % on 4:8 weights, -8 % on
 // paired ones).
 // Shorter ones (30B-class prefill, 1e11) lose more to the second launch
@@ -1104,12 +1105,17 @@ static moesq_status_t launch_layout(SpgemmArgs a, bool swiglu, hipStream_t strea
     return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
                   : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
   }
-  // otherwise two launches, split by each expert's own row count (read on
-  // the device): up to 32 rows the two-fragment streaming tile, above it
-  // the contraction tile
+  // otherwise launches split by each expert's own row count (read on the
+  // device): up to 16 rows the one-fragment streaming tile, up to 32 the
+  // two-fragment one, above that the contraction tile
+  a.rows_hi = 16;
+  moesq_status_t st = swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
+                             : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
+  if (st != MOESQ_OK) return st;
+  a.rows_lo = 16;
   a.rows_hi = 32;
-  moesq_status_t st = swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
-                             : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  st = swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
+              : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
   if (st != MOESQ_OK) return st;
   a.rows_lo = 32;
   a.rows_hi = INT_MAX;

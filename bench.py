@@ -8,8 +8,10 @@ device-resident input:
   route -> dispatch + grouped GEMM (gate/up, SwiGLU epilogue) -> grouped GEMM
   (down) -> router-weighted combine            (trillion-class workloads)
   route -> dispatch + grouped GEMM -> combine  (30B-class workloads)
-The dispatch (gather of the routed token rows) runs inside the first GEMM;
---unfused runs it as its own permute kernel instead.
+The dispatch (gather of the routed token rows) runs inside the first GEMM,
+and for decode batches (T*k <= 1024 and <= 4E) the routing too
+(moesq_route_grouped_spgemm); --unfused runs route and permute as kernels of
+their own.
 Inputs (tokens, top-k ids, router weights, packed expert weights) are built
 and packed on the GPU before timing.  Every step replays a HIP graph of its
 launches; the timed region is bracketed by a device synchronisation on both
@@ -55,7 +57,8 @@ ROTATE_BYTES = 1 << 30        # weight replicas rotate until they span 1 GiB
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: enough for about 0.25 s of timed work, 20 to 4000)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill-1t", choices=list(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -63,6 +66,8 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--unfused", action="store_true",
                     help="run the dispatch as its own permute kernel instead of inside the first GEMM")
+    ap.add_argument("--separate-route", action="store_true",
+                    help="decode batches: keep routing in its own kernel instead of the first GEMM")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of steps: time the first grouped GEMM of --workload over a grid "
                          "of active-expert counts G x rows per expert R (one JSON line per point)")
@@ -140,7 +145,7 @@ def pack_on_gpu(m, wl, proj, chunk=16, paired=False):
 class Step:
     """Buffers and launches of one pass of the hot path."""
 
-    def __init__(self, m, wl, fused=True, paired=False):
+    def __init__(self, m, wl, fused=True, paired=False, separate_route=False):
         self.m, self.wl, self.fused = m, wl, fused
         dev = torch.device("cuda")
         ids, tw = synth.routing(wl)
@@ -173,8 +178,10 @@ class Step:
         else:
             self.y = torch.empty(M, wl.proj[0][1], **bf)
         self.out = torch.empty(T if wl.weighted_combine else M, self.y.shape[1], **bf)
-        self.names = (["route"] + ([] if fused else ["permute"]) + [f"gemm_{p[0]}" for p in wl.proj]
-                      + ["combine"])
+        # decode batches route inside the first GEMM's launch
+        self.route_in_gemm = fused and not separate_route and M <= 1024 and M <= 4 * E
+        self.names = (([] if self.route_in_gemm else ["route"]) + ([] if fused else ["permute"])
+                      + [f"gemm_{p[0]}" for p in wl.proj] + ["combine"])
 
     def calls(self):
         """(name, launch) of every kernel of one step, on the next weight
@@ -182,15 +189,19 @@ class Step:
         m, wl = self.m, self.wl
         w = self.replicas[self.turn % len(self.replicas)]
         self.turn += 1
-        calls = [
-            lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm, self.inv,
-                                  self.route_ws),
-        ]
+        calls = []
+        if not self.route_in_gemm:
+            calls.append(lambda: m.moesq_route(self.ids, wl.T, wl.k, wl.E, self.off, self.perm,
+                                               self.inv, self.route_ws))
         if not self.fused:
             calls.append(lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr))
 
         def first(epi, out):
-            # dispatch fused into the first GEMM, or the routed copy
+            # routing and dispatch fused into the first GEMM, dispatch fused,
+            # or the routed copy
+            if self.route_in_gemm:
+                return lambda: m.moesq_route_grouped_spgemm(self.ids, self.x, wl.T, wl.k, w[0], epi,
+                                                            out, self.off, self.perm, self.inv)
             if self.fused:
                 return lambda: m.moesq_grouped_spgemm_gather(self.x, self.perm, wl.T, wl.k, self.off,
                                                              w[0], epi, out)
@@ -438,7 +449,8 @@ def main():
         sweep(m, wl, Gs=tuple(int(v) for v in args.sweep_experts.split(",")),
               Rs=tuple(int(v) for v in args.sweep_rows.split(",")), paired=args.paired)
         return
-    step = Step(m, wl, fused=not args.unfused, paired=args.paired)
+    step = Step(m, wl, fused=not args.unfused, paired=args.paired,
+                separate_route=args.separate_route)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -448,6 +460,15 @@ def main():
     graphs = step.capture_steps()
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
+    if args.steps is None:
+        # short steps are timed over more replays, long ones over at least 20
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(len(graphs)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        est = (time.perf_counter() - t) / len(graphs)
+        args.steps = int(min(4000, max(20, 0.25 / max(est, 1e-6))))
     # Timed region: exactly `steps` steps, synchronised on both sides.
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -71,6 +71,8 @@ typedef enum {
 
 /* Limits of this build. */
 #define MOESQ_MAX_EXPERTS 1024
+/* Largest T*k that moesq_route_grouped_spgemm routes inside the GEMM launch. */
+#define MOESQ_FUSED_ROUTE_MAX_ROWS 1024
 
 /*
  * Compressed expert weights, canonical layout.  For expert e (0 <= e < E),
@@ -222,6 +224,31 @@ moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const int32_t *per
                                            int32_t k, const int32_t *expert_offsets,
                                            const moesq_weights_t *w, int32_t epilogue, uint16_t *y,
                                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Routing, dispatch and grouped GEMM of a decode batch in one launch: the
+ * results of moesq_route(topk_ids, T, k, E, expert_offsets, perm, inv_perm,
+ * ...) followed by moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets,
+ * w, epilogue, y, ...), bit for bit.  Every workgroup of the GEMM builds the
+ * routing plan of the T*k ids in LDS (the same stable counting sort) and
+ * workgroup 0 stores it, so the plan is there for moesq_unpermute.  The
+ * pages keep routing outside the expert kernel ("D.3 End-to-end serving
+ * benchmark"); for decode batches the separate routing launch and its gap
+ * cost as much as a fifth of a 30B-class step, hence this fused form.
+ *   topk_ids [T*k] int32; x [T][K] bf16; w, epilogue, y as
+ *   moesq_grouped_spgemm_gather; expert_offsets [E+1], perm [T*k],
+ *   inv_perm [T*k] int32 out (as moesq_route; perm and inv_perm may be NULL
+ *   when T*k == 0).
+ * One launch when 0 < T*k <= MOESQ_FUSED_ROUTE_MAX_ROWS and T*k <= 4*E (a
+ * decode batch); otherwise the call makes the two separate calls above
+ * (moesq_route without workspace, then the gather GEMM).
+ * Limits: those of moesq_route (1 <= k <= E) and of
+ *         moesq_grouped_spgemm_gather.
+ */
+moesq_status_t moesq_route_grouped_spgemm(const int32_t *topk_ids, const uint16_t *x, int32_t T,
+                                          int32_t k, const moesq_weights_t *w, int32_t epilogue,
+                                          uint16_t *y, int32_t *expert_offsets, int32_t *perm,
+                                          int32_t *inv_perm, hipStream_t stream);
 
 /*
  * Combine.

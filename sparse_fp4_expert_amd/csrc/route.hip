@@ -22,65 +22,12 @@
 // kernel over (block, expert) counts in the workspace, and a scatter kernel
 // per block.
 #include "common.hpp"
+#include "route_dev.hpp"
 
 namespace moesq {
 
 constexpr int ROUTE_WAVES = 8;
 constexpr int ROUTE_THREADS = ROUTE_WAVES * 64;
-
-__device__ __forceinline__ uint64_t peers_of(int e, int nbits, uint64_t active) {
-  uint64_t peers = active;
-#pragma unroll 1
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bal = __ballot(bit);
-    peers &= bit ? bal : ~bal;
-  }
-  return peers;
-}
-
-// Histogram of ids[beg, end) into cnt[e] by one wave (leaders add).
-__device__ __forceinline__ void wave_count(const int32_t *__restrict__ ids, int beg, int end,
-                                           int E, int nbits, uint64_t lt_mask, int lane,
-                                           int *cnt) {
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    int e = -1;
-    if (i < end) {
-      e = ids[i];
-      if (e < 0 || e >= E) e = -1;
-    }
-    const uint64_t active = __ballot(e >= 0);
-    const uint64_t peers = peers_of(e, nbits, active);
-    if (e >= 0 && (peers & lt_mask) == 0) cnt[e] += __popcll(peers);
-  }
-}
-
-// Ranks and scatter of ids[beg, end) by one wave; run[e] holds the next
-// routed row of expert e for this wave and advances.
-__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int beg, int end,
-                                             int E, int nbits, uint64_t lt_mask, int lane,
-                                             int *run, int32_t *perm, int32_t *inv_perm) {
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    int e = -1;
-    if (i < end) {
-      e = ids[i];
-      if (e < 0 || e >= E) e = -1;
-    }
-    const uint64_t active = __ballot(e >= 0);
-    const uint64_t peers = peers_of(e, nbits, active);
-    int row = -1;
-    if (e >= 0) row = run[e] + __popcll(peers & lt_mask);
-    // all lanes have read run[e]; leaders now advance it
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0 && (peers & lt_mask) == 0) run[e] += __popcll(peers);
-    if (i < end) {
-      inv_perm[i] = row;
-      if (row >= 0) perm[row] = i;
-    }
-  }
-}
 
 // Exclusive prefix of v[0..n) in place by the whole block; returns the total.
 template <int THREADS>
@@ -114,11 +61,6 @@ __device__ int block_exclusive_scan(int *v, int n, int *wave_tot) {
   }
   __syncthreads();
   return tot;
-}
-
-__device__ __forceinline__ int id_bits(int E) { return (E > 1) ? 32 - __clz(E - 1) : 0; }
-__device__ __forceinline__ uint64_t lanes_below(int lane) {
-  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Whole plan in one workgroup.

@@ -1,0 +1,71 @@
+// Wave-level pieces of the routing plan (stable counting sort of the flat
+// top-k ids), shared by the routing kernels and by the grouped GEMM's fused
+// routing prologue.  See route.hip for the method.
+#pragma once
+
+#include "common.hpp"
+
+namespace moesq {
+
+__device__ __forceinline__ uint64_t peers_of(int e, int nbits, uint64_t active) {
+  uint64_t peers = active;
+#pragma unroll 1
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  return peers;
+}
+
+// Histogram of ids[beg, end) into cnt[e] by one wave (leaders add).
+__device__ __forceinline__ void wave_count(const int32_t *__restrict__ ids, int beg, int end,
+                                           int E, int nbits, uint64_t lt_mask, int lane,
+                                           int *cnt) {
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    int e = -1;
+    if (i < end) {
+      e = ids[i];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t active = __ballot(e >= 0);
+    const uint64_t peers = peers_of(e, nbits, active);
+    if (e >= 0 && (peers & lt_mask) == 0) cnt[e] += __popcll(peers);
+  }
+}
+
+// Ranks and scatter of ids[beg, end) by one wave; run[e] holds the next
+// routed row of expert e for this wave and advances.  inv_perm may be NULL
+// (not written).
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int beg, int end,
+                                             int E, int nbits, uint64_t lt_mask, int lane,
+                                             int *run, int32_t *perm, int32_t *inv_perm) {
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    int e = -1;
+    if (i < end) {
+      e = ids[i];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t active = __ballot(e >= 0);
+    const uint64_t peers = peers_of(e, nbits, active);
+    int row = -1;
+    if (e >= 0) row = run[e] + __popcll(peers & lt_mask);
+    // all lanes have read run[e]; leaders now advance it
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && (peers & lt_mask) == 0) run[e] += __popcll(peers);
+    if (i < end) {
+      if (inv_perm) inv_perm[i] = row;
+      if (row >= 0) perm[row] = i;
+    }
+  }
+}
+
+__device__ __forceinline__ int id_bits(int E) { return (E > 1) ? 32 - __clz(E - 1) : 0; }
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+
+}  // namespace moesq

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "route_dev.hpp"
 
 namespace moesq {
 
@@ -49,6 +50,10 @@ struct SpgemmArgs {
   int M, E, N, K;
   int row_tiles;
   int rows_lo, rows_hi;     // this launch takes the experts with rows_lo < rows <= rows_hi
+  // fused routing (decode batches): the flat top-k ids [M]; every workgroup
+  // builds the plan in LDS, workgroup 0 also stores it
+  const int32_t *ids;
+  int32_t *route_offsets, *route_perm, *route_inv;
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -372,11 +377,11 @@ enum { FMT_CANONICAL = 0, FMT_TILED = 1, FMT_PAIRED = 2 };
 
 // Dynamic LDS of the item schedule for E experts: prefix [E+1] and row
 // counts [E] as int, partial-tile experts [E] as uint16, rounded to 16 bytes.
-static inline size_t spgemm_sched_bytes(int E) {
+__host__ __device__ inline size_t spgemm_sched_bytes(int E) {
   return ((size_t)(2 * E + 1) * 4 + (size_t)E * 2 + 15) & ~(size_t)15;
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false>
 __global__ __launch_bounds__(WAVES * 64)
 // 16-row tiles stream weights: at most 128 VGPRs, so that four 4-wave
 // workgroups share a CU.  32-row tiles hold 128 accumulators per lane.
@@ -438,9 +443,55 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
                                               // [E] experts with a partial tile, costly first
 
   if constexpr (!PAIRED) build_group_lut(lut);
+  // Fused routing: the routing plan of the M flat ids (offsets, gather
+  // permutation), built by wave 0 in LDS after the schedule arrays, exactly
+  // as moesq_route builds it (stable counting sort); workgroup 0 also
+  // stores it for the combine.
+  int *const s_roff = s_dyn + spgemm_sched_bytes(E) / 4;   // [E+1]
+  int *const s_run = s_roff + E + 1;                        // [E]
+  int *const s_rperm = s_run + E;                           // [M]
+  if constexpr (ROUTE) {
+    for (int e = tid; e < E; e += WAVES * 64) s_run[e] = 0;
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t lt = lanes_below(lane);
+      const int nbits = id_bits(E);
+      wave_count(a.ids, 0, M, E, nbits, lt, lane, s_run);
+      // exclusive prefix of the counts over the experts
+      const int per = (E + 63) / 64;
+      const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+      int sum = 0;
+      for (int e = e0; e < e1; ++e) sum += s_run[e];
+      int incl = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      int run = incl - sum;
+      for (int e = e0; e < e1; ++e) {
+        const int c = s_run[e];
+        s_roff[e] = run;
+        s_run[e] = run;
+        run += c;
+      }
+      if (lane == 63) s_roff[E] = incl;
+      __builtin_amdgcn_wave_barrier();
+      wave_scatter(a.ids, 0, M, E, nbits, lt, lane, s_run, s_rperm,
+                   blockIdx.x == 0 ? a.route_inv : nullptr);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int e = tid; e <= E; e += WAVES * 64) a.route_offsets[e] = s_roff[e];
+      for (int r = tid; r < s_roff[E]; r += WAVES * 64) a.route_perm[r] = s_rperm[r];
+    }
+  }
   // expert row ranges straight from the offsets (clamped to [0, M]); only
   // the item prefix is kept in LDS
-  auto off_at = [&](int e) { return min(max(a.offsets[e], 0), M); };
+  auto off_at = [&](int e) {
+    return min(max(ROUTE ? s_roff[e] : a.offsets[e], 0), M);
+  };
+  auto perm_at = [&](int r) { return ROUTE ? s_rperm[r] : a.perm[r]; };
   // routed rows per expert; experts outside this launch's row range count as
   // empty (another launch of the same call takes them)
   for (int e = tid; e < E; e += WAVES * 64) {
@@ -672,8 +723,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     for (int j = 0; j < BPW; ++j) {
       const int r = tok0 + min((wave * BPW + j) * (64 / UPR) + lane / UPR, ntok - 1);
       int src = r;
-      if (a.perm) {
-        const int pi = a.perm[r];
+      if (ROUTE || a.perm) {
+        const int pi = perm_at(r);
         src = (pi >= 0 && pi < a.T * a.k) ? pi / a.k : 0;
       }
       srow[j] = (uint32_t)src * (uint32_t)K;
@@ -973,8 +1024,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         if (trow >= ntok) continue;
         const size_t out_r = (size_t)(tok0 + trow);
         bool keep = true;
-        if (a.perm) {
-          const int pi = a.perm[out_r];
+        if (ROUTE || a.perm) {
+          const int pi = perm_at((int)out_r);
           keep = pi >= 0 && pi < a.T * a.k;
         }
   #pragma unroll
@@ -1029,12 +1080,13 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false>
 static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
-  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT>;
+  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT, ROUTE>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-  const size_t dyn = spgemm_sched_bytes(a.E);
+  // schedule arrays, then with fused routing its offsets, cursors and permutation
+  const size_t dyn = spgemm_sched_bytes(a.E) + (ROUTE ? (size_t)(2 * a.E + 1 + a.M) * 4 : 0);
   // upper bound of the item count: every expert may hold one partial tile
   const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
   // workgroups per CU for this dynamic LDS size (cached per device and size)
@@ -1207,6 +1259,73 @@ extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
   (void)ws_bytes;
   return spgemm_entry("moesq_grouped_spgemm", x_routed, nullptr, 0, 1, expert_offsets, M, w,
                       epilogue, y, stream);
+}
+
+// Fused routing + dispatch + grouped GEMM of a decode batch.
+template <int FMT>
+static moesq_status_t launch_routed(const SpgemmArgs &a, bool swiglu, hipStream_t stream) {
+  return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT, true>(a, stream)
+                : launch_one<4, 16, 2, 1, 256, false, FMT, true>(a, stream);
+}
+
+extern "C" moesq_status_t moesq_route_grouped_spgemm(const int32_t *topk_ids, const uint16_t *x,
+                                                     int32_t T, int32_t k,
+                                                     const moesq_weights_t *w, int32_t epilogue,
+                                                     uint16_t *y, int32_t *expert_offsets,
+                                                     int32_t *perm, int32_t *inv_perm,
+                                                     hipStream_t stream) {
+  static const char *who = "moesq_route_grouped_spgemm";
+  clear_error();
+  moesq_status_t st = check_weights(w, who);
+  if (st != MOESQ_OK) return st;
+  if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffll)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": need T >= 0, k >= 1, T*k < 2^31");
+  if (k > w->E) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": need k <= E");
+  if (epilogue != MOESQ_EPI_NONE && epilogue != MOESQ_EPI_SWIGLU)
+    return fail(MOESQ_ERR_ARG, std::string(who) + ": unknown epilogue");
+  if (epilogue == MOESQ_EPI_SWIGLU && w->N % 32)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": SwiGLU needs N % 32 == 0");
+  if (!expert_offsets) return fail(MOESQ_ERR_NULL, std::string(who) + ": expert_offsets is NULL");
+  const int M = T * k;
+  if (M > 0 && (!topk_ids || !x || !y || !perm || !inv_perm))
+    return fail(MOESQ_ERR_NULL,
+                std::string(who) + ": NULL ids, tokens, output rows or routing output");
+  if ((long long)T * w->K > 0x7fffffffll)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": rows of x times K must stay under 2^31");
+  if (M == 0 || M > MOESQ_FUSED_ROUTE_MAX_ROWS || (long long)M > 4ll * w->E) {
+    // not a decode batch: the plan by moesq_route, then the gather GEMM
+    st = moesq_route(topk_ids, T, k, w->E, expert_offsets, perm, inv_perm, nullptr, 0, stream);
+    if (st != MOESQ_OK) return st;
+    return moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets, w, epilogue, y, nullptr,
+                                       0, stream);
+  }
+  SpgemmArgs a{};
+  a.x = x;
+  a.perm = nullptr;
+  a.T = T;
+  a.k = k;
+  a.offsets = nullptr;
+  a.values = w->values;
+  a.masks = w->masks;
+  a.scales = w->scales;
+  a.gscale = w->global_scale;
+  a.y = y;
+  a.M = M;
+  a.E = w->E;
+  a.N = w->N;
+  a.K = w->K;
+  a.rows_lo = 0;
+  a.rows_hi = INT_MAX;
+  a.ids = topk_ids;
+  a.route_offsets = expert_offsets;
+  a.route_perm = perm;
+  a.route_inv = inv_perm;
+  const bool sw = epilogue == MOESQ_EPI_SWIGLU;
+  switch (w->layout) {
+    case MOESQ_LAYOUT_TILED: return launch_routed<FMT_TILED>(a, sw, stream);
+    case MOESQ_LAYOUT_PAIRED_TILED: return launch_routed<FMT_PAIRED>(a, sw, stream);
+    default: return launch_routed<FMT_CANONICAL>(a, sw, stream);
+  }
 }
 
 extern "C" moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const int32_t *perm,

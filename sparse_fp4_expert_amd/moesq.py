@@ -52,6 +52,8 @@ _spgemm = _sig("moesq_grouped_spgemm", _i32, _vp, _vp, _i32, ctypes.POINTER(Weig
 _spgemm_ws = _sig("moesq_spgemm_workspace_bytes", _sz, _i32, ctypes.POINTER(WeightsDesc))
 _spgemm_gather = _sig("moesq_grouped_spgemm_gather", _i32, _vp, _vp, _i32, _i32, _vp,
                       ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _sz, _vp)
+_route_spgemm = _sig("moesq_route_grouped_spgemm", _i32, _vp, _vp, _i32, _i32,
+                     ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _vp, _vp, _vp)
 _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _pack_paired = _sig("moesq_pack_weights_paired", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -67,7 +69,7 @@ _version = _sig("moesq_version", _i32)
 
 EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes",
-            "moesq_grouped_spgemm_gather", "moesq_unpermute",
+            "moesq_grouped_spgemm_gather", "moesq_route_grouped_spgemm", "moesq_unpermute",
             "moesq_pack_weights", "moesq_pack_weights_paired", "moesq_tile_weights",
             "moesq_decode_weights",
             "moesq_validate", "moesq_stream_read", "moesq_status_string",
@@ -197,6 +199,15 @@ def moesq_grouped_spgemm_gather(x, perm, T: int, k: int, expert_offsets, w: Weig
                           0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def moesq_route_grouped_spgemm(topk_ids, x, T: int, k: int, w: Weights, epilogue: int, y,
+                               expert_offsets, perm, inv_perm, stream=None):
+    _check(_route_spgemm(_ptr(topk_ids, torch.int32, "topk_ids", True), _ptr(x, torch.bfloat16, "x", True),
+                         T, k, ctypes.byref(w.desc), epilogue, _ptr(y, torch.bfloat16, "y", True),
+                         _ptr(expert_offsets, torch.int32, "expert_offsets"),
+                         _ptr(perm, torch.int32, "perm", True), _ptr(inv_perm, torch.int32, "inv_perm", True),
+                         _stream(stream)))
+
+
 def moesq_spgemm_workspace_bytes(M: int, w: Weights) -> int:
     return int(_spgemm_ws(M, ctypes.byref(w.desc)))
 
@@ -298,6 +309,22 @@ def grouped_spgemm_gather(x, perm, k: int, expert_offsets, w: Weights, epilogue:
         out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=x.device)
     moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets, w, epilogue, out, None, stream)
     return out
+
+
+def route_grouped_spgemm(topk_ids, x, k: int, w: Weights, epilogue: int = EPI_NONE, out=None,
+                         stream=None):
+    """Routing, dispatch and GEMM of a decode batch in one launch.  Returns
+    (out [T*k, N or N/2], expert_offsets [E+1], perm [T*k], inv_perm [T*k])."""
+    T = x.shape[0]
+    dev = x.device
+    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    if out is None:
+        out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=dev)
+    off = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    moesq_route_grouped_spgemm(topk_ids, x, T, k, w, epilogue, out, off, perm, inv, stream)
+    return out, off, perm, inv
 
 
 def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):

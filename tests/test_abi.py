@@ -164,3 +164,17 @@ def test_stream_read_rejects(m):
     assert sr(0x10, 24, 0x10, None) == m.ERR_ARG      # bytes % 16
     assert sr(0x18, 16, 0x10, None) == m.ERR_ARG      # misaligned buffer
     assert sr(0x10, 0, 0x10, None) == m.OK            # nothing to read
+
+
+def test_route_spgemm_rejects(m):
+    ref = ctypes.byref
+    f = m._route_spgemm
+    d = ref(_desc(m))
+    assert f(0x10, 0x10, 4, 2, None, 0, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_NULL     # descriptor
+    assert f(0x10, 0x10, -1, 2, d, 0, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE      # T < 0
+    assert f(0x10, 0x10, 4, 0, d, 0, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE       # k < 1
+    assert f(0x10, 0x10, 4, 9, ref(_desc(m, E=8)), 0, 0x10, 0x10, 0x10, 0x10,
+             None) == m.ERR_SHAPE                                                       # k > E
+    assert f(0x10, 0x10, 4, 2, d, 5, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_ARG         # epilogue
+    assert f(0x10, 0x10, 4, 2, d, 0, 0x10, None, 0x10, 0x10, None) == m.ERR_NULL        # offsets
+    assert f(None, 0x10, 4, 2, d, 0, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_NULL        # ids

@@ -7,11 +7,12 @@ One step is one pass of the whole hot path over one batch of synthetic,
 device-resident input:
   route -> dispatch + grouped GEMM (gate/up, SwiGLU epilogue) -> grouped GEMM
   (down) -> router-weighted combine            (trillion-class workloads)
-  route -> dispatch + grouped GEMM -> combine  (30B-class workloads)
+  route -> dispatch + grouped GEMM -> scatter to flat order  (30B-class workloads)
 The dispatch (gather of the routed token rows) runs inside the first GEMM,
 and for decode batches (T*k <= 1024 and <= 4E) the routing too
-(moesq_route_grouped_spgemm); --unfused runs route and permute as kernels of
-their own.
+(moesq_route_grouped_spgemm); the 30B-class scatter (no router weights) is
+the GEMM's epilogue storing each row at its flat position (MOESQ_OUT_FLAT).
+--unfused runs route, permute and the scatter as kernels of their own.
 Inputs (tokens, top-k ids, router weights, packed expert weights) are built
 and packed on the GPU before timing.  Every step replays a HIP graph of its
 launches; the timed region is bracketed by a device synchronisation on both
@@ -180,8 +181,12 @@ class Step:
         self.out = torch.empty(T if wl.weighted_combine else M, self.y.shape[1], **bf)
         # decode batches route inside the first GEMM's launch
         self.route_in_gemm = fused and not separate_route and M <= 1024 and M <= 4 * E
+        # without router weights the combine is a pure scatter to flat order:
+        # with dispatch fused, the GEMM's epilogue stores there directly
+        self.scatter_in_gemm = fused and not wl.weighted_combine and not wl.swiglu
         self.names = (([] if self.route_in_gemm else ["route"]) + ([] if fused else ["permute"])
-                      + [f"gemm_{p[0]}" for p in wl.proj] + ["combine"])
+                      + [f"gemm_{p[0]}" for p in wl.proj]
+                      + ([] if self.scatter_in_gemm else ["combine"]))
 
     def calls(self):
         """(name, launch) of every kernel of one step, on the next weight
@@ -211,11 +216,14 @@ class Step:
             calls.append(first(m.EPI_SWIGLU, self.h))
             calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, w[1],
                                                         m.EPI_NONE, self.y))
+        elif self.scatter_in_gemm:
+            calls.append(first(m.EPI_NONE | m.OUT_FLAT, self.out))
         else:
             calls.append(first(m.EPI_NONE, self.y))
-        tw = self.tw if wl.weighted_combine else None
-        calls.append(lambda: m.moesq_unpermute(self.y, self.inv, tw, wl.T, wl.k,
-                                               self.y.shape[1], self.out))
+        if not self.scatter_in_gemm:
+            tw = self.tw if wl.weighted_combine else None
+            calls.append(lambda: m.moesq_unpermute(self.y, self.inv, tw, wl.T, wl.k,
+                                                   self.y.shape[1], self.out))
         return list(zip(self.names, calls))
 
     def run(self):

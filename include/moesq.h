@@ -64,6 +64,21 @@ typedef enum {
   MOESQ_EPI_SWIGLU = 1  /* y[r][c] = bf16(silu(g_e*acc[r][c]) * g_e*acc[r][c+N/2]), c<N/2 */
 } moesq_epilogue_t;
 
+/*
+ * Output-order flag, OR-ed into the epilogue argument of
+ * moesq_grouped_spgemm_gather and moesq_route_grouped_spgemm: result row r
+ * (routed order) is stored at y[perm[r]], i.e. y comes out in flat order
+ * t*k + j, the order moesq_unpermute without weights produces from the
+ * routed rows -- the scatter after the expert GEMM fused into its epilogue
+ * ("D.1 Implementation details": the serving kernels fuse dispatch and
+ * scatter with the first expert GEMM).  Same values, bit for bit; rows r
+ * whose perm[r] is outside [0, T*k) are not stored anywhere, so with a
+ * valid routing (perm a permutation of [0, T*k)) every row of y is written
+ * exactly once.  moesq_grouped_spgemm (no permutation) rejects the flag with
+ * MOESQ_ERR_ARG.
+ */
+#define MOESQ_OUT_FLAT 0x100
+
 #define MOESQ_LAYOUT_CANONICAL 0
 #define MOESQ_LAYOUT_TILED 1
 #define MOESQ_LAYOUT_PAIRED 2

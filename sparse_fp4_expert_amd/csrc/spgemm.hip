@@ -54,6 +54,7 @@ struct SpgemmArgs {
   // builds the plan in LDS, workgroup 0 also stores it
   const int32_t *ids;
   int32_t *route_offsets, *route_perm, *route_inv;
+  int flat;   // store result row r at y[perm[r]] (flat order) instead of y[r]
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -1022,11 +1023,15 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       for (int t = 0; t < NF; ++t) {
         const int trow = t * MS + rl;
         if (trow >= ntok) continue;
-        const size_t out_r = (size_t)(tok0 + trow);
+        size_t out_r = (size_t)(tok0 + trow);
         bool keep = true;
         if (ROUTE || a.perm) {
           const int pi = perm_at((int)out_r);
           keep = pi >= 0 && pi < a.T * a.k;
+          if (a.flat) {   // scatter to the flat position; no destination: no store
+            if (!keep) continue;
+            out_r = (size_t)pi;
+          }
         }
   #pragma unroll
         for (int r4 = 0; r4 < MF::NC / 4; ++r4) {
@@ -1221,8 +1226,12 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   clear_error();
   moesq_status_t st = check_weights(w, who);
   if (st != MOESQ_OK) return st;
+  const bool flat = (epilogue & MOESQ_OUT_FLAT) != 0;
+  epilogue &= ~MOESQ_OUT_FLAT;
   if (epilogue != MOESQ_EPI_NONE && epilogue != MOESQ_EPI_SWIGLU)
     return fail(MOESQ_ERR_ARG, std::string(who) + ": unknown epilogue");
+  if (flat && !perm)
+    return fail(MOESQ_ERR_ARG, std::string(who) + ": MOESQ_OUT_FLAT needs the gather permutation");
   if (epilogue == MOESQ_EPI_SWIGLU && w->N % 32)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": SwiGLU needs N % 32 == 0");
   if (M < 0) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": M must be >= 0");
@@ -1247,6 +1256,7 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   a.E = w->E;
   a.N = w->N;
   a.K = w->K;
+  a.flat = flat;
   return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout, stream);
 }
 
@@ -1281,9 +1291,10 @@ extern "C" moesq_status_t moesq_route_grouped_spgemm(const int32_t *topk_ids, co
   if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffll)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": need T >= 0, k >= 1, T*k < 2^31");
   if (k > w->E) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": need k <= E");
-  if (epilogue != MOESQ_EPI_NONE && epilogue != MOESQ_EPI_SWIGLU)
+  const int32_t epi = epilogue & ~MOESQ_OUT_FLAT;
+  if (epi != MOESQ_EPI_NONE && epi != MOESQ_EPI_SWIGLU)
     return fail(MOESQ_ERR_ARG, std::string(who) + ": unknown epilogue");
-  if (epilogue == MOESQ_EPI_SWIGLU && w->N % 32)
+  if (epi == MOESQ_EPI_SWIGLU && w->N % 32)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": SwiGLU needs N % 32 == 0");
   if (!expert_offsets) return fail(MOESQ_ERR_NULL, std::string(who) + ": expert_offsets is NULL");
   const int M = T * k;
@@ -1320,7 +1331,8 @@ extern "C" moesq_status_t moesq_route_grouped_spgemm(const int32_t *topk_ids, co
   a.route_offsets = expert_offsets;
   a.route_perm = perm;
   a.route_inv = inv_perm;
-  const bool sw = epilogue == MOESQ_EPI_SWIGLU;
+  a.flat = (epilogue & MOESQ_OUT_FLAT) != 0;
+  const bool sw = epi == MOESQ_EPI_SWIGLU;
   switch (w->layout) {
     case MOESQ_LAYOUT_TILED: return launch_routed<FMT_TILED>(a, sw, stream);
     case MOESQ_LAYOUT_PAIRED_TILED: return launch_routed<FMT_PAIRED>(a, sw, stream);

@@ -24,6 +24,9 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_LAYOUT, ERR_HIP, ERR_ARG = 0, -1, -2, -3, -4, -5, -6
 EPI_NONE, EPI_SWIGLU = 0, 1
+# OR-ed into the epilogue of the gather and fused-routing GEMMs: rows come out
+# in flat order (row r stored at y[perm[r]]), the scatter fused into the GEMM.
+OUT_FLAT = 0x100
 LAYOUT_CANONICAL, LAYOUT_TILED, LAYOUT_PAIRED, LAYOUT_PAIRED_TILED = 0, 1, 2, 3
 PAIRED_LAYOUTS = (LAYOUT_PAIRED, LAYOUT_PAIRED_TILED)
 MAX_EXPERTS = 1024
@@ -293,7 +296,7 @@ def permute(x, perm, k: int, stream=None):
 def grouped_spgemm(x_routed, expert_offsets, w: Weights, epilogue: int = EPI_NONE, out=None,
                    stream=None):
     M = x_routed.shape[0]
-    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
     if out is None:
         out = torch.empty(M, n_out, dtype=torch.bfloat16, device=x_routed.device)
     moesq_grouped_spgemm(x_routed, expert_offsets, M, w, epilogue, out, None, stream)
@@ -302,9 +305,10 @@ def grouped_spgemm(x_routed, expert_offsets, w: Weights, epilogue: int = EPI_NON
 
 def grouped_spgemm_gather(x, perm, k: int, expert_offsets, w: Weights, epilogue: int = EPI_NONE,
                           out=None, stream=None):
-    """Dispatch fused into the GEMM: routed row r reads token perm[r] // k of x."""
+    """Dispatch fused into the GEMM: routed row r reads token perm[r] // k of x
+    (with OUT_FLAT in `epilogue`, row r is stored at out[perm[r]])."""
     T = x.shape[0]
-    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
     if out is None:
         out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=x.device)
     moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets, w, epilogue, out, None, stream)
@@ -317,7 +321,7 @@ def route_grouped_spgemm(topk_ids, x, k: int, w: Weights, epilogue: int = EPI_NO
     (out [T*k, N or N/2], expert_offsets [E+1], perm [T*k], inv_perm [T*k])."""
     T = x.shape[0]
     dev = x.device
-    n_out = w.N // 2 if epilogue == EPI_SWIGLU else w.N
+    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
     if out is None:
         out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=dev)
     off = torch.empty(w.E + 1, dtype=torch.int32, device=dev)

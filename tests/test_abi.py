@@ -88,6 +88,10 @@ def test_spgemm_rejects(m):
     big = _desc(m, N=1 << 16, K=1 << 17)                       # one expert's values = 2 GiB
     assert g(0x10, ok_off, 4, ref(big), 0, 0x10, None, 0, None) == m.ERR_SHAPE
     assert g(0x10, ok_off, 4, ref(_desc(m)), 5, 0x10, None, 0, None) == m.ERR_ARG          # epilogue
+    # flat output order needs a gather permutation, which this call has not
+    assert g(0x10, ok_off, 4, ref(_desc(m)), m.OUT_FLAT, 0x10, None, 0, None) == m.ERR_ARG
+    assert b"MOESQ_OUT_FLAT" in m._last_error()
+    assert g(0x10, ok_off, 4, ref(_desc(m)), m.OUT_FLAT | 5, 0x10, None, 0, None) == m.ERR_ARG
     assert g(0x10, None, 4, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_NULL
     assert g(0x10, ok_off, -1, ref(_desc(m)), 0, 0x10, None, 0, None) == m.ERR_SHAPE
     assert g(None, ok_off, 0, ref(_desc(m)), 0, None, None, 0, None) == m.OK                # M = 0
@@ -128,6 +132,7 @@ def test_spgemm_gather_rejects(m):
     assert g(0x10, 0x10, 4, 2, None, d, 0, 0x10, None, 0, None) == m.ERR_NULL        # offsets NULL
     assert g(0x10, 0x10, 4, 2, 0x10, ref(_desc(m, layout=7)), 0, 0x10, None, 0, None) == m.ERR_LAYOUT
     assert g(0x10, 0x10, 4, 2, 0x10, d, 5, 0x10, None, 0, None) == m.ERR_ARG         # epilogue
+    assert g(0x10, 0x10, 4, 2, 0x10, d, m.OUT_FLAT | 2, 0x10, None, 0, None) == m.ERR_ARG
     assert g(None, None, 0, 2, 0x10, d, 0, None, None, 0, None) == m.OK              # T = 0
 
 

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t *__r
 
 constexpr int RB_WAVES = 4;
 constexpr int RB_THREADS = RB_WAVES * 64;
-constexpr int ROUTE_BLOCK_IDS = 2048;          // ids per block, 512 per wave
+constexpr int ROUTE_BLOCK_IDS = 512;           // ids per block, 128 per wave
 
 // Large inputs, step 1: counts[b][e] of block b.
 __global__ __launch_bounds__(RB_THREADS) void route_hist_kernel(const int32_t *__restrict__ ids,
@@ -132,35 +132,42 @@ __global__ __launch_bounds__(RB_THREADS) void route_hist_kernel(const int32_t *_
   }
 }
 
-// Step 2 (one workgroup): counts[b][e] -> first routed row of block b's
-// ids of expert e; offsets.
+// Step 2 (one workgroup): counts[b][e] -> number of ids of expert e in the
+// blocks before b (the first routed row of block b's ids of expert e is
+// offsets[e] plus that); offsets.
 __global__ __launch_bounds__(ROUTE_THREADS) void route_scan_kernel(int *counts, int nb, int E,
                                                                    int32_t *offsets) {
   __shared__ int tot[MOESQ_MAX_EXPERTS + 1];
   __shared__ int wave_tot[ROUTE_WAVES];
+  // the counts of SCAN_BATCH blocks are loaded before any is rewritten, so
+  // that the loads of a batch overlap instead of one load-store round trip
+  // per block
+  constexpr int SCAN_BATCH = 8;
   for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = counts[(size_t)b * E + e];
-      counts[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += SCAN_BATCH) {
+      int c[SCAN_BATCH];
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j)
+        c[j] = b0 + j < nb ? counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j) {
+        if (b0 + j < nb) counts[(size_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
     tot[e] = run;
   }
   __syncthreads();
   const int total = block_exclusive_scan<ROUTE_THREADS>(tot, E, wave_tot);
-  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
-    const int o = tot[e];
-    offsets[e] = o;
-    for (int b = 0; b < nb; ++b) counts[(size_t)b * E + e] += o;
-  }
+  for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) offsets[e] = tot[e];
   if (threadIdx.x == 0) offsets[E] = total;
 }
 
 // Step 3: ranks inside block b on top of its bases; perm and inv_perm.
 __global__ __launch_bounds__(RB_THREADS) void route_scatter_kernel(
-    const int32_t *__restrict__ ids, int M, int E, const int *bases, int32_t *perm,
-    int32_t *inv_perm) {
+    const int32_t *__restrict__ ids, int M, int E, const int *bases, const int32_t *offsets,
+    int32_t *perm, int32_t *inv_perm) {
   __shared__ int cnt[RB_WAVES][MOESQ_MAX_EXPERTS];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nbits = id_bits(E);
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(RB_THREADS) void route_scatter_kernel(
   wave_count(ids, beg, end, E, nbits, lt_mask, lane, cnt[w]);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += RB_THREADS) {
-    int run = bases[(size_t)blockIdx.x * E + e];
+    int run = bases[(size_t)blockIdx.x * E + e] + offsets[e];
 #pragma unroll
     for (int v = 0; v < RB_WAVES; ++v) {
       const int c = cnt[v][e];
@@ -228,6 +235,6 @@ extern "C" moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, counts, nb, E,
                      expert_offsets);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids,
-                     (int)M, E, counts, perm, inv_perm);
+                     (int)M, E, counts, expert_offsets, perm, inv_perm);
   return launch_status("moesq_route");
 }

@@ -145,7 +145,8 @@ def test_route_workloads(lib, name):
 
 @pytest.mark.parametrize("E,M,k,mode", [
     (1, 64, 1, "random"), (8, 1, 1, "random"), (8, 640, 4, "same"), (1024, 70000, 2, "random"),
-    (384, 65536, 8, "skew"), (5, 63, 3, "random"), (2, 129, 1, "random")])
+    (384, 65536, 8, "skew"), (5, 63, 3, "random"), (2, 129, 1, "random"),
+    (384, 1000008, 8, "skew")])   # 1954 blocks: a partial batch of block counts and a partial last block
 def test_route_edges(lib, E, M, k, mode):
     rng = np.random.default_rng(E * 7 + M)
     if mode == "same":

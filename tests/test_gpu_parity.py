@@ -208,7 +208,7 @@ def test_permute(lib, name):
     assert torch.equal(xr.cpu(), x[torch.from_numpy(pref.astype(np.int64)) // wl.k])
 
 
-@pytest.mark.parametrize("T,k,N", [(64, 2, 128), (1024, 8, 7168), (5, 3, 8)])
+@pytest.mark.parametrize("T,k,N", [(64, 2, 128), (1024, 8, 7168), (5, 3, 8), (37, 10, 136)])
 def test_unpermute(lib, T, k, N):
     E = max(k, 16)
     rng = np.random.default_rng(T + N)

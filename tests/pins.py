@@ -339,6 +339,110 @@ def pin_swiglu(O):
     assert np.allclose(h, [[0.0, 3.0 / (1.0 + math.exp(-1.0))]], rtol=1e-15)
 
 
+
+# ---------------------------------------------------------------- the expert chain
+
+def _fixture_rows(d, prefix, n):
+    return np.array([[float(v) for v in d[f"{prefix}{i}"]] for i in range(n)], np.float64)
+
+
+def pin_chain_fixture(O):
+    """The hand-derived chain (tests/golden/chain_rows.txt): routing, Y1, the
+    bf16 hidden activation h, Y2 and the router-weighted combine of two tokens
+    over two experts, every value derived by hand from the inputs."""
+    d = {ln[0]: ln[1:] for ln in _lines("chain_rows.txt")}
+    x = _fixture_rows(d, "x", 2)
+    ids = np.array([int(v) for v in d["ids"]], np.int32)
+    tw = np.array([float(v) for v in d["topk_weights"]], np.float32)
+    up = [np.array([float(v) for v in d[f"up{e}"]], np.float64).reshape(4, 2) for e in range(2)]
+    down = [np.array([float(v) for v in d[f"down{e}"]], np.float64).reshape(4, 2) for e in range(2)]
+    off, perm, inv = O.route(ids, 2)
+    assert off.tolist() == [0, 2, 4] and perm.tolist() == [1, 2, 0, 3] and inv.tolist() == [2, 0, 1, 3]
+    y1, h, y2, out = O.moe_chain(x, off, perm, inv, 2, lambda e: up[e], lambda e: down[e], tw)
+    assert np.array_equal(y1, _fixture_rows(d, "y1_r", 4)), y1
+    assert np.array_equal(h, _fixture_rows(d, "h_r", 4)), h
+    assert np.array_equal(y2, _fixture_rows(d, "y2_r", 4)), y2
+    assert np.array_equal(out, _fixture_rows(d, "out", 2)), out
+
+
+def _bf16_exact(v: Fraction) -> Fraction:
+    """Round a rational to the nearest value with 8 significant bits, ties to
+    even (exact; no floating point)."""
+    if v == 0:
+        return Fraction(0)
+    s = -1 if v < 0 else 1
+    a, e = abs(v), 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    q = a * 128
+    n = math.floor(q)
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2):
+        n += 1
+    return s * Fraction(n, 128) * Fraction(2) ** e
+
+
+def pin_chain_bruteforce(O, seed=13):
+    """The chain on compressed experts against exact rational arithmetic in
+    plain loops: Y1 and Y2 as exact sums, h as the exact bf16 rounding of
+    silu(gate) * up (silu by math.exp), the combine as exact weighted sums.
+    The oracle's float64 results must lie within their summation bounds, and
+    h must equal the exact rounding except within 1e-12 of a rounding
+    midpoint (where either neighbour is right)."""
+    rng = np.random.default_rng(seed)
+    E, T, k, K, N1, N2 = 3, 5, 2, 64, 64, 16
+    up = [O.decode(O.quantize((rng.standard_normal((N1, K)) * 0.5).astype(np.float32)))
+          for _ in range(E)]
+    down = [O.decode(O.quantize((rng.standard_normal((N2, N1 // 2)) * 0.5).astype(np.float32)))
+            for _ in range(E)]
+    x = torch.randn(T, K, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    x = x.to(torch.float64).numpy()
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).reshape(-1).astype(np.int32)
+    tw = rng.random(T * k).astype(np.float32)
+    off, perm, inv = O.route(ids, E)
+    y1, h, y2, out = O.moe_chain(x, off, perm, inv, k, lambda e: up[e], lambda e: down[e], tw)
+    u = 2.0 ** -53
+    y2_exact = {}
+    for t in range(T):
+        for j in range(k):
+            i = t * k + j
+            e = int(ids[i])
+            r = int(inv[i])
+            assert perm[r] == i
+            xf = [Fraction(float(v)) for v in x[t]]
+            y1e = [sum(xf[c] * Fraction(float(up[e][n, c])) for c in range(K)) for n in range(N1)]
+            for n in range(N1):
+                mag = sum(abs(xf[c] * Fraction(float(up[e][n, c]))) for c in range(K))
+                assert abs(Fraction(float(y1[r, n])) - y1e[n]) <= Fraction(K * u) * mag + Fraction(1, 2 ** 1074)
+            he = []
+            for c in range(N1 // 2):
+                g = float(y1e[c])
+                v = Fraction(g / (1.0 + math.exp(-g))) * y1e[c + N1 // 2]
+                want = _bf16_exact(v)
+                got = Fraction(float(h[r, c]))
+                if got != want:
+                    # only a value at a rounding midpoint may go either way
+                    lo, hi = sorted([got, want])
+                    mid = (lo + hi) / 2
+                    assert abs(v - mid) <= Fraction(1, 10 ** 12) * abs(v), (r, c, float(v), float(got))
+                he.append(got)
+            y2e = [sum(he[c] * Fraction(float(down[e][n, c])) for c in range(N1 // 2)) for n in range(N2)]
+            for n in range(N2):
+                mag = sum(abs(he[c] * Fraction(float(down[e][n, c]))) for c in range(N1 // 2))
+                assert abs(Fraction(float(y2[r, n])) - y2e[n]) <= Fraction(N1 * u) * mag + Fraction(1, 2 ** 1074)
+            y2_exact[i] = (y2e, [sum(abs(he[c] * Fraction(float(down[e][n, c]))) for c in range(N1 // 2))
+                                 for n in range(N2)])
+    for t in range(T):
+        for n in range(N2):
+            want = sum(Fraction(float(tw[t * k + j])) * y2_exact[t * k + j][0][n] for j in range(k))
+            mag = sum(Fraction(float(tw[t * k + j])) * y2_exact[t * k + j][1][n] for j in range(k))
+            assert abs(Fraction(float(out[t, n])) - want) <= Fraction((N1 + 2 * k) * u) * mag + Fraction(1, 2 ** 1074), (t, n)
+
+
 # ---------------------------------------------------------------- paired 4:8
 
 def pin_paired_fixture(O):
@@ -447,4 +551,4 @@ ALL_PINS = [pin_e2m1_grid, pin_e4m3_table, pin_e4m3_encode, pin_e2m1_encode,
             pin_masks_and_layout, pin_quant_nearest, pin_route_bruteforce,
             pin_gemm_exact, pin_gemm_invariances, pin_unpermute, pin_swiglu,
             pin_paired_fixture, pin_paired_support_bruteforce, pin_paired_layout,
-            pin_paired_matches_48]
+            pin_paired_matches_48, pin_chain_fixture, pin_chain_bruteforce]

@@ -173,3 +173,61 @@ def test_paired_decode_pair_offset(monkeypatch):
                         lambda p: (3 << (6 - 2 * oracle.PAIRS[p][0])) | (3 << (6 - 2 * oracle.PAIRS[p][1])))
     _fails(pins.pin_paired_matches_48, oracle)
     _fails(pins.pin_paired_fixture, oracle)
+
+
+# ---------------------------------------------------------------- the expert chain
+
+import oracle.moe  # noqa: E402
+
+_CHAIN_PINS = (pins.pin_chain_fixture, pins.pin_chain_bruteforce)
+
+
+def _chain_fails(O):
+    for pin in _CHAIN_PINS:
+        _fails(pin, O)
+
+
+def test_chain_h_not_rounded(monkeypatch):
+    # the hidden activation kept in float64 instead of crossing as bf16
+    monkeypatch.setattr(oracle.moe, "bf16_round", lambda v: np.asarray(v, np.float64))
+    _chain_fails(oracle)
+
+
+def test_chain_down_fed_gate_half():
+    # the down GEMM fed Y1's gate half instead of h
+    def chain(x, off, perm, inv, k, w_up, w_down, tw=None):
+        xr = oracle.permute(np.asarray(x, np.float64), perm, k)
+        y1 = oracle.grouped_gemm(xr, off, w_up)
+        h = oracle.bf16_round(oracle.swiglu(y1))
+        y2 = oracle.grouped_gemm(y1[:, :y1.shape[1] // 2], off, w_down)
+        return y1, h, y2, oracle.unpermute(y2, inv, tw, x.shape[0], k)
+    _chain_fails(_ns(moe_chain=chain))
+
+
+def test_chain_weights_swapped():
+    def chain(x, off, perm, inv, k, w_up, w_down, tw=None):
+        return oracle.moe_chain(x, off, perm, inv, k, w_down, w_up, tw)
+    # the fixture's projections have the same shape; the brute-force case
+    # does not, so its run raises before any comparison
+    _fails(pins.pin_chain_fixture, _ns(moe_chain=chain))
+    with pytest.raises(Exception):
+        pins.pin_chain_bruteforce(_ns(moe_chain=chain))
+
+
+def test_chain_unweighted_combine():
+    def chain(x, off, perm, inv, k, w_up, w_down, tw=None):
+        ones = None if tw is None else np.ones_like(np.asarray(tw))
+        return oracle.moe_chain(x, off, perm, inv, k, w_up, w_down, ones)
+    _chain_fails(_ns(moe_chain=chain))
+
+
+def test_chain_silu_on_up_half():
+    # SwiGLU halves swapped inside the chain
+    def chain(x, off, perm, inv, k, w_up, w_down, tw=None):
+        xr = oracle.permute(np.asarray(x, np.float64), perm, k)
+        y1 = oracle.grouped_gemm(xr, off, w_up)
+        n2 = y1.shape[1] // 2
+        h = oracle.bf16_round(oracle.silu(y1[:, n2:]) * y1[:, :n2])
+        y2 = oracle.grouped_gemm(h, off, w_down)
+        return y1, h, y2, oracle.unpermute(y2, inv, tw, x.shape[0], k)
+    _chain_fails(_ns(moe_chain=chain))

@@ -110,6 +110,23 @@ def _ptr(t, dtype, name, allow_none=False):
     return t.data_ptr() if t.numel() else None
 
 
+def _sizes(*checks):
+    """Raises ValueError unless every (tensor, elements, name) matches: the
+    library sizes its loads and stores from the shape arguments, so a tensor
+    of another size would be read or written out of bounds on the device.
+    A None tensor is skipped (the C call decides whether it may be NULL)."""
+    for t, n, name in checks:
+        if t is None or not isinstance(t, torch.Tensor):
+            continue
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements ({tuple(t.shape)}), "
+                             f"the shape arguments need {n}")
+
+
+def _out_cols(w, epilogue: int) -> int:
+    return w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -169,6 +186,8 @@ class Weights:
 
 def moesq_route(topk_ids, T: int, k: int, E: int, expert_offsets, perm, inv_perm,
                 ws=None, stream=None):
+    _sizes((topk_ids, T * k, "topk_ids"), (expert_offsets, E + 1, "expert_offsets"),
+           (perm, T * k, "perm"), (inv_perm, T * k, "inv_perm"))
     _check(_route(_ptr(topk_ids, torch.int32, "topk_ids"), T, k, E,
                   _ptr(expert_offsets, torch.int32, "expert_offsets"),
                   _ptr(perm, torch.int32, "perm"), _ptr(inv_perm, torch.int32, "inv_perm"),
@@ -181,12 +200,15 @@ def moesq_route_workspace_bytes(T: int, k: int, E: int) -> int:
 
 
 def moesq_permute(x, perm, T: int, k: int, K: int, x_routed, stream=None):
+    _sizes((x, T * K, "x"), (perm, T * k, "perm"), (x_routed, T * k * K, "x_routed"))
     _check(_permute(_ptr(x, torch.bfloat16, "x"), _ptr(perm, torch.int32, "perm"), T, k, K,
                     _ptr(x_routed, torch.bfloat16, "x_routed"), _stream(stream)))
 
 
 def moesq_grouped_spgemm(x_routed, expert_offsets, M: int, w: Weights, epilogue: int, y,
                          ws=None, stream=None):
+    _sizes((x_routed, M * w.K, "x_routed"), (expert_offsets, w.E + 1, "expert_offsets"),
+           (y, M * _out_cols(w, epilogue), "y"))
     _check(_spgemm(_ptr(x_routed, torch.bfloat16, "x_routed"),
                    _ptr(expert_offsets, torch.int32, "expert_offsets"), M,
                    ctypes.byref(w.desc), epilogue, _ptr(y, torch.bfloat16, "y"),
@@ -196,6 +218,8 @@ def moesq_grouped_spgemm(x_routed, expert_offsets, M: int, w: Weights, epilogue:
 
 def moesq_grouped_spgemm_gather(x, perm, T: int, k: int, expert_offsets, w: Weights,
                                 epilogue: int, y, ws=None, stream=None):
+    _sizes((x, T * w.K, "x"), (perm, T * k, "perm"), (expert_offsets, w.E + 1, "expert_offsets"),
+           (y, T * k * _out_cols(w, epilogue), "y"))
     _check(_spgemm_gather(_ptr(x, torch.bfloat16, "x"), _ptr(perm, torch.int32, "perm"), T, k,
                           _ptr(expert_offsets, torch.int32, "expert_offsets"), ctypes.byref(w.desc),
                           epilogue, _ptr(y, torch.bfloat16, "y"), _ptr(ws, torch.uint8, "ws", True),
@@ -204,6 +228,9 @@ def moesq_grouped_spgemm_gather(x, perm, T: int, k: int, expert_offsets, w: Weig
 
 def moesq_route_grouped_spgemm(topk_ids, x, T: int, k: int, w: Weights, epilogue: int, y,
                                expert_offsets, perm, inv_perm, stream=None):
+    _sizes((topk_ids, T * k, "topk_ids"), (x, T * w.K, "x"),
+           (y, T * k * _out_cols(w, epilogue), "y"), (expert_offsets, w.E + 1, "expert_offsets"),
+           (perm, T * k, "perm"), (inv_perm, T * k, "inv_perm"))
     _check(_route_spgemm(_ptr(topk_ids, torch.int32, "topk_ids", True), _ptr(x, torch.bfloat16, "x", True),
                          T, k, ctypes.byref(w.desc), epilogue, _ptr(y, torch.bfloat16, "y", True),
                          _ptr(expert_offsets, torch.int32, "expert_offsets"),
@@ -216,6 +243,9 @@ def moesq_spgemm_workspace_bytes(M: int, w: Weights) -> int:
 
 
 def moesq_unpermute(y, inv_perm, topk_weights, T: int, k: int, N: int, out, stream=None):
+    rows = T if topk_weights is not None else T * k
+    _sizes((y, T * k * N, "y"), (inv_perm, T * k, "inv_perm"),
+           (topk_weights, T * k, "topk_weights"), (out, rows * N, "out"))
     _check(_unpermute(_ptr(y, torch.bfloat16, "y"), _ptr(inv_perm, torch.int32, "inv_perm"),
                       _ptr(topk_weights, torch.float32, "topk_weights", True), T, k, N,
                       _ptr(out, torch.bfloat16, "out"), _stream(stream)))
@@ -223,6 +253,9 @@ def moesq_unpermute(y, inv_perm, topk_weights, T: int, k: int, N: int, out, stre
 
 def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, global_scale,
                        stream=None):
+    _sizes((dense, E * N * K, "dense"), (values, E * N * K // 4, "values"),
+           (masks, E * N * K // 8, "masks"), (scales, E * N * K // 32, "scales"),
+           (global_scale, E, "global_scale"))
     _check(_pack(_ptr(dense, torch.float32, "dense"), E, N, K, _ptr(values, torch.uint8, "values"),
                  _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
                  _ptr(global_scale, torch.float32, "global_scale"), _stream(stream)))
@@ -230,6 +263,9 @@ def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, glo
 
 def moesq_pack_weights_paired(dense, E: int, N: int, K: int, values, patterns, scales,
                               global_scale, stream=None):
+    _sizes((dense, E * N * K, "dense"), (values, E * N * K // 4, "values"),
+           (patterns, E * N * K // 16, "patterns"), (scales, E * N * K // 32, "scales"),
+           (global_scale, E, "global_scale"))
     _check(_pack_paired(_ptr(dense, torch.float32, "dense"), E, N, K,
                         _ptr(values, torch.uint8, "values"), _ptr(patterns, torch.uint8, "patterns"),
                         _ptr(scales, torch.uint8, "scales"),
@@ -237,12 +273,15 @@ def moesq_pack_weights_paired(dense, E: int, N: int, K: int, values, patterns, s
 
 
 def moesq_tile_weights(src: Weights, values, masks, scales, stream=None):
+    _sizes((values, src.values.numel(), "values"), (masks, src.masks.numel(), "masks"),
+           (scales, src.scales.numel(), "scales"))
     _check(_tile(ctypes.byref(src.desc), _ptr(values, torch.uint8, "values"),
                  _ptr(masks, torch.uint8, "masks"), _ptr(scales, torch.uint8, "scales"),
                  _stream(stream)))
 
 
 def moesq_decode_weights(w: Weights, expert: int, dense, stream=None):
+    _sizes((dense, w.N * w.K, "dense"))
     _check(_decode(ctypes.byref(w.desc), expert, _ptr(dense, torch.bfloat16, "dense"),
                    _stream(stream)))
 
@@ -255,6 +294,7 @@ def moesq_validate(topk_ids=None, T: int = 0, k: int = 1, E: int = 1, expert_off
     """Debug check of the caller contracts (synchronises).  Returns the
     violation count of each check; a failed check is not an exception (the
     counts say which), bad sizes and HIP failures are."""
+    _sizes((topk_ids, T * k, "topk_ids"), (expert_offsets, E + 1, "expert_offsets"))
     counts = (ctypes.c_uint64 * len(VALIDATE_CHECKS))()
     st = _validate(_ptr(topk_ids, torch.int32, "topk_ids", True), T, k, E,
                    _ptr(expert_offsets, torch.int32, "expert_offsets", True),
@@ -276,6 +316,8 @@ def moesq_stream_read(buf, sink, stream=None):
 def route(topk_ids, E: int, k: int, stream=None):
     """Returns (expert_offsets [E+1], perm [M], inv_perm [M]) as int32 device tensors."""
     M = topk_ids.numel()
+    if M % k:
+        raise ValueError(f"topk_ids has {M} entries, not a multiple of k = {k}")
     dev = topk_ids.device
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(M, dtype=torch.int32, device=dev)
@@ -287,6 +329,8 @@ def route(topk_ids, E: int, k: int, stream=None):
 
 
 def permute(x, perm, k: int, stream=None):
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, K], got {tuple(x.shape)}")
     T, K = x.shape
     out = torch.empty(T * k, K, dtype=torch.bfloat16, device=x.device)
     moesq_permute(x, perm, T, k, K, out, stream)
@@ -295,10 +339,14 @@ def permute(x, perm, k: int, stream=None):
 
 def grouped_spgemm(x_routed, expert_offsets, w: Weights, epilogue: int = EPI_NONE, out=None,
                    stream=None):
+    if x_routed.dim() != 2 or x_routed.shape[1] != w.K:
+        raise ValueError(f"x_routed must be [M, {w.K}], got {tuple(x_routed.shape)}")
     M = x_routed.shape[0]
-    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
+    n_out = _out_cols(w, epilogue)
     if out is None:
         out = torch.empty(M, n_out, dtype=torch.bfloat16, device=x_routed.device)
+    elif tuple(out.shape) != (M, n_out):
+        raise ValueError(f"out must be [{M}, {n_out}], got {tuple(out.shape)}")
     moesq_grouped_spgemm(x_routed, expert_offsets, M, w, epilogue, out, None, stream)
     return out
 
@@ -307,10 +355,14 @@ def grouped_spgemm_gather(x, perm, k: int, expert_offsets, w: Weights, epilogue:
                           out=None, stream=None):
     """Dispatch fused into the GEMM: routed row r reads token perm[r] // k of x
     (with OUT_FLAT in `epilogue`, row r is stored at out[perm[r]])."""
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [T, {w.K}], got {tuple(x.shape)}")
     T = x.shape[0]
-    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
+    n_out = _out_cols(w, epilogue)
     if out is None:
         out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=x.device)
+    elif tuple(out.shape) != (T * k, n_out):
+        raise ValueError(f"out must be [{T * k}, {n_out}], got {tuple(out.shape)}")
     moesq_grouped_spgemm_gather(x, perm, T, k, expert_offsets, w, epilogue, out, None, stream)
     return out
 
@@ -319,11 +371,15 @@ def route_grouped_spgemm(topk_ids, x, k: int, w: Weights, epilogue: int = EPI_NO
                          stream=None):
     """Routing, dispatch and GEMM of a decode batch in one launch.  Returns
     (out [T*k, N or N/2], expert_offsets [E+1], perm [T*k], inv_perm [T*k])."""
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [T, {w.K}], got {tuple(x.shape)}")
     T = x.shape[0]
     dev = x.device
-    n_out = w.N // 2 if (epilogue & ~OUT_FLAT) == EPI_SWIGLU else w.N
+    n_out = _out_cols(w, epilogue)
     if out is None:
         out = torch.empty(T * k, n_out, dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != (T * k, n_out):
+        raise ValueError(f"out must be [{T * k}, {n_out}], got {tuple(out.shape)}")
     off = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
@@ -332,6 +388,8 @@ def route_grouped_spgemm(topk_ids, x, k: int, w: Weights, epilogue: int = EPI_NO
 
 
 def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):
+    if y.dim() != 2 or y.shape[0] != T * k:
+        raise ValueError(f"y must be [T*k = {T * k}, N], got {tuple(y.shape)}")
     N = y.shape[1]
     rows = T if topk_weights is not None else T * k
     out = torch.empty(rows, N, dtype=torch.bfloat16, device=y.device)
@@ -341,6 +399,8 @@ def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):
 
 def pack_weights(dense, stream=None, paired: bool = False) -> Weights:
     """dense float32 [E, N, K] on the GPU -> canonical (or paired) Weights."""
+    if dense.dim() != 3:
+        raise ValueError(f"dense must be [E, N, K], got {tuple(dense.shape)}")
     E, N, K = dense.shape
     w = Weights.empty(E, N, K, device=dense.device,
                       layout=LAYOUT_PAIRED if paired else LAYOUT_CANONICAL)

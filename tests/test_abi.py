@@ -183,3 +183,72 @@ def test_route_spgemm_rejects(m):
     assert f(0x10, 0x10, 4, 2, d, 5, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_ARG         # epilogue
     assert f(0x10, 0x10, 4, 2, d, 0, 0x10, None, 0x10, 0x10, None) == m.ERR_NULL        # offsets
     assert f(None, 0x10, 4, 2, d, 0, 0x10, 0x10, 0x10, 0x10, None) == m.ERR_NULL        # ids
+
+
+# ---------------------------------------------------------------- binding size checks
+
+def _fake_weights(m, E=8, N=128, K=256):
+    """A weight descriptor stand-in on the CPU (the size checks run before any
+    pointer is taken)."""
+    import types
+    return types.SimpleNamespace(E=E, N=N, K=K, desc=_desc(m, E, N, K))
+
+
+def test_binding_rejects_mismatched_sizes(m):
+    """Every mirror of a C call compares the tensors' element counts with the
+    shape arguments before any pointer reaches the library, so a mismatched
+    tensor raises ValueError instead of being read or written out of bounds."""
+    import torch
+    i32, bf, u8, f32 = torch.int32, torch.bfloat16, torch.uint8, torch.float32
+    z = lambda *s, dt=i32: torch.zeros(*s, dtype=dt)          # noqa: E731
+    w = _fake_weights(m)
+    T, k, E, K, N = 4, 2, 8, 256, 128
+    cases = [
+        lambda: m.moesq_route(z(T * k + 1), T, k, E, z(E + 1), z(T * k), z(T * k)),
+        lambda: m.moesq_route(z(T * k), T, k, E, z(E), z(T * k), z(T * k)),
+        lambda: m.moesq_route(z(T * k), T, k, E, z(E + 1), z(T * k), z(T * k - 1)),
+        lambda: m.moesq_permute(z(T, K + 8, dt=bf), z(T * k), T, k, K, z(T * k, K, dt=bf)),
+        lambda: m.moesq_permute(z(T, K, dt=bf), z(T * k), T, k, K, z(T * k - 1, K, dt=bf)),
+        lambda: m.moesq_grouped_spgemm(z(T * k, K - 32, dt=bf), z(E + 1), T * k, w, 0,
+                                       z(T * k, N, dt=bf)),
+        lambda: m.moesq_grouped_spgemm(z(T * k, K, dt=bf), z(E + 1), T * k, w, 0,
+                                       z(T * k, N // 2, dt=bf)),          # plain epilogue: N cols
+        lambda: m.moesq_grouped_spgemm(z(T * k, K, dt=bf), z(E + 1), T * k, w, m.EPI_SWIGLU,
+                                       z(T * k, N, dt=bf)),               # SwiGLU: N/2 cols
+        lambda: m.moesq_grouped_spgemm(z(T * k, K, dt=bf), z(E + 2), T * k, w, 0,
+                                       z(T * k, N, dt=bf)),
+        lambda: m.moesq_grouped_spgemm_gather(z(T + 1, K, dt=bf), z(T * k), T, k, z(E + 1), w, 0,
+                                              z(T * k, N, dt=bf)),
+        lambda: m.moesq_grouped_spgemm_gather(z(T, K, dt=bf), z(T), T, k, z(E + 1), w, 0,
+                                              z(T * k, N, dt=bf)),
+        lambda: m.moesq_route_grouped_spgemm(z(T * k), z(T, K, dt=bf), T, k, w, 0,
+                                             z(T, N, dt=bf), z(E + 1), z(T * k), z(T * k)),
+        lambda: m.moesq_route_grouped_spgemm(z(T * k), z(T, K, dt=bf), T, k, w, 0,
+                                             z(T * k, N, dt=bf), z(E + 1), z(T * k), z(T)),
+        lambda: m.moesq_unpermute(z(T * k, N, dt=bf), z(T * k), z(T * k, dt=f32), T, k, N,
+                                  z(T * k, N, dt=bf)),                    # weighted: T rows
+        lambda: m.moesq_unpermute(z(T * k, N, dt=bf), z(T * k), None, T, k, N,
+                                  z(T, N, dt=bf)),                        # flat: T*k rows
+        lambda: m.moesq_unpermute(z(T * k, N + 8, dt=bf), z(T * k), None, T, k, N,
+                                  z(T * k, N, dt=bf)),
+        lambda: m.moesq_pack_weights(z(1, 16, 64, dt=f32), 1, 16, 64, z(1, 16, 15, dt=u8),
+                                     z(1, 16, 8, dt=u8), z(1, 16, 2, dt=u8), z(1, dt=f32)),
+        lambda: m.moesq_pack_weights_paired(z(1, 16, 64, dt=f32), 1, 16, 64, z(1, 16, 16, dt=u8),
+                                            z(1, 16, 8, dt=u8), z(1, 16, 2, dt=u8), z(1, dt=f32)),
+        lambda: m.moesq_decode_weights(w, 0, z(N, K - 1, dt=bf)),
+        # convenience wrappers: operand shapes against the weights
+        lambda: m.grouped_spgemm(z(T * k, K + 64, dt=bf), z(E + 1), w),
+        lambda: m.grouped_spgemm(z(T * k, K, dt=bf), z(E + 1), w, out=z(T * k + 1, N, dt=bf)),
+        lambda: m.grouped_spgemm_gather(z(T, K // 2, dt=bf), z(T * k), k, z(E + 1), w),
+        lambda: m.grouped_spgemm_gather(z(T, K, dt=bf), z(T * k), k, z(E + 1), w,
+                                        out=z(T * k, N, dt=bf), epilogue=m.EPI_SWIGLU),
+        lambda: m.route_grouped_spgemm(z(T * k), z(T, K - 32, dt=bf), k, w),
+        lambda: m.unpermute(z(T * k + 2, N, dt=bf), z(T * k), None, T, k),
+        lambda: m.route(z(T * k + 1), E, k),
+        lambda: m.permute(z(T * K, dt=bf), z(T * k), k),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError) as ei:
+            case()
+        msg = str(ei.value)
+        assert "on the GPU" not in msg, (i, msg)

@@ -94,11 +94,11 @@ struct WChunk {
 // vb/mb/sb: the expert's value/mask/scale bases; fv/fm/fs: byte offsets of
 // each fragment's first row (uniform); vo/mo/so: this lane's offsets inside
 // a fragment (its row and lane group); kv/km/ks: offsets of the chunk.
-// ok[f]: the lane's first scale block lies inside K; two-block ranges load
-// only the first block when `whole` is false (K ends in the middle of the
-// range).
-template <int RF, int KQ>
-__device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb,
+// ok[f]: the lane's first scale block lies inside K; the two-block range
+// loads only its first block when `whole` is false (K ends in the middle of
+// the range).
+template <int RF>
+__device__ __forceinline__ void load_wchunk(WChunk<RF, 64> &w, const uint8_t *vb,
                                             const uint8_t *mb, const uint8_t *sb,
                                             const uint32_t (&fv)[RF], const uint32_t (&fm)[RF],
                                             const uint32_t (&fs)[RF], uint32_t vo, uint32_t mo,
@@ -106,46 +106,36 @@ __device__ __forceinline__ void load_wchunk(WChunk<RF, KQ> &w, const uint8_t *vb
                                             uint32_t kv, uint32_t km, uint32_t ks) {
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
-    if (KQ == 64 && ok[f] && !whole) {
-      const uint8_t *pv = vb + (fv[f] + vo + kv);
-      const uint8_t *pm = mb + (fm[f] + mo + km);
-      const uint8_t *ps = sb + (fs[f] + so + ks);
+    if (!ok[f]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w.v[f][i] = 0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) w.m[f][i] = 0;
+      w.s[f] = 0;
+      continue;
+    }
+    const uint8_t *pv = vb + (fv[f] + vo + kv);
+    const uint8_t *pm = mb + (fm[f] + mo + km);
+    const uint8_t *ps = sb + (fs[f] + so + ks);
+    if (!whole) {
       const uint2 v = *reinterpret_cast<const uint2 *>(pv);
       w.v[f][0] = v.x;
       w.v[f][1] = v.y;
-#pragma unroll
-      for (int i = 2; i < WChunk<RF, KQ>::VD; ++i) w.v[f][i] = 0;
+      w.v[f][2] = 0;
+      w.v[f][3] = 0;
       w.m[f][0] = *reinterpret_cast<const uint32_t *>(pm);
-#pragma unroll
-      for (int i = 1; i < WChunk<RF, KQ>::MD; ++i) w.m[f][i] = 0;
+      w.m[f][1] = 0;
       w.s[f] = *ps;
-    } else if (ok[f]) {
-      const uint8_t *pv = vb + (fv[f] + vo + kv);
-      const uint8_t *pm = mb + (fm[f] + mo + km);
-      const uint8_t *ps = sb + (fs[f] + so + ks);
-      if constexpr (KQ == 32) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(pv);
-        w.v[f][0] = v.x;
-        w.v[f][1] = v.y;
-        w.m[f][0] = *reinterpret_cast<const uint32_t *>(pm);
-        w.s[f] = *ps;
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4 *>(pv);
-        w.v[f][0] = v.x;
-        w.v[f][1] = v.y;
-        w.v[f][2] = v.z;
-        w.v[f][3] = v.w;
-        const uint2 m = *reinterpret_cast<const uint2 *>(pm);
-        w.m[f][0] = m.x;
-        w.m[f][1] = m.y;
-        w.s[f] = *reinterpret_cast<const uint16_t *>(ps);
-      }
     } else {
-#pragma unroll
-      for (int i = 0; i < WChunk<RF, KQ>::VD; ++i) w.v[f][i] = 0;
-#pragma unroll
-      for (int i = 0; i < WChunk<RF, KQ>::MD; ++i) w.m[f][i] = 0;
-      w.s[f] = 0;
+      const uint4 v = *reinterpret_cast<const uint4 *>(pv);
+      w.v[f][0] = v.x;
+      w.v[f][1] = v.y;
+      w.v[f][2] = v.z;
+      w.v[f][3] = v.w;
+      const uint2 m = *reinterpret_cast<const uint2 *>(pm);
+      w.m[f][0] = m.x;
+      w.m[f][1] = m.y;
+      w.s[f] = *reinterpret_cast<const uint16_t *>(ps);
     }
   }
 }
@@ -199,17 +189,14 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
   constexpr int KQ = KC * MS / 64;
   constexpr int S = KQ / 8;
   constexpr int UPR = KC / 8;
+  static_assert(KQ == 64, "a lane group covers two scale blocks per chunk");
   // block scales: the hardware E4M3 (OCP) conversion is exact
-  float sf[RF][KQ / 32];
+  float sf[RF][2];
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
-    if constexpr (KQ == 64) {
-      const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.s[f], 1.0f, false);
-      sf[f][0] = p[0];
-      sf[f][1] = p[1];
-    } else {
-      sf[f][0] = __builtin_amdgcn_cvt_f32_fp8(w.s[f], 0);
-    }
+    const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.s[f], 1.0f, false);
+    sf[f][0] = p[0];
+    sf[f][1] = p[1];
   }
   const uint16_t *brow = tk + rl * KC;
   const int cbase = (KQ / 8) * q;
@@ -401,8 +388,7 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   static_assert(NBLK % WAVES == 0, "token tile must split evenly over the waves");
   static_assert(64 % UPR == 0, "a 1 KB load covers whole token rows");
   static_assert(RF % 2 == 0, "SwiGLU pairs gate and up fragments");
-  static_assert(KQ == 32 || KQ == 64, "a lane group covers one or two scale blocks");
-  static_assert(!TILED || KQ == 64, "tiled weights give each lane group one 64-position segment");
+  static_assert(KQ == 64, "a lane group covers one 64-position segment (two scale blocks) per chunk");
 
   __shared__ uint4 lut[PAIRED ? 1 : 256];   // 4:8 selector table (paired needs none)
   // Item order (contraction tiles): every expert's whole token tiles first

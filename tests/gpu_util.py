@@ -68,3 +68,38 @@ def assert_same_pack(w, e: int, p, what=""):
     assert np.array_equal(w.masks[e].cpu().numpy(), meta), f"{what}: masks/patterns differ"
     assert np.array_equal(w.scales[e].cpu().numpy(), p.scales), f"{what}: scales differ"
     assert w.global_scale[e].item() == float(p.g), f"{what}: global scale differs"
+
+
+# Large grouped-GEMM calls split the experts over three launches by their own
+# row counts: up to 16 rows, 17 to 32, and more.  Samples cover each range.
+LAUNCH_RANGES = ((1, 16), (17, 32), (33, 1 << 30))
+
+
+def pick_experts(counts, rng, n_random=1):
+    """Experts to check: the largest, one from each launch range's row counts
+    (the middle one of the range, in expert order), and a few random active
+    ones."""
+    active = np.nonzero(counts)[0]
+    pick = {int(active[np.argmax(counts[active])])}
+    for lo, hi in LAUNCH_RANGES:
+        inr = active[(counts[active] >= lo) & (counts[active] <= hi)]
+        if len(inr):
+            pick.add(int(inr[len(inr) // 2]))
+    for e in rng.choice(active, size=min(n_random, len(active)), replace=False):
+        pick.add(int(e))
+    return sorted(pick)
+
+
+def oracle_experts(wl, proj: int, experts, paired: bool = False, threads: int = 16):
+    """The oracle's compression and exact float64 decode of the given experts
+    (dense weights drawn on the GPU exactly as pack_workload draws them), run
+    on a pool of host threads.  Returns {e: (packed, decoded)}."""
+    import concurrent.futures as cf
+    dense = {int(e): synth.dense_expert(wl, proj, int(e), device="cuda").cpu().numpy()
+             for e in experts}
+
+    def one(e):
+        p = oracle.quantize_paired(dense[e]) if paired else oracle.quantize(dense[e])
+        return e, (p, oracle_decode(p))
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(one, list(dense)))

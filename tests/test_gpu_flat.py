@@ -1,19 +1,25 @@
 """Scatter fused into the GEMM epilogue (MOESQ_OUT_FLAT): the gather GEMM
 and the fused routing + GEMM with rows stored at y[perm[r]] give exactly
-the routed-order result followed by moesq_unpermute without weights (flat
-order), for 4:8 and paired weights, plain and SwiGLU epilogues, at the
-workload shapes and on a batch with invalid routing entries."""
+the routed-order result reordered to flat order by the oracle's combine
+without weights (float64 on the host), for 4:8 and paired weights, plain and
+SwiGLU epilogues, at the workload shapes and on a batch with invalid routing
+entries."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from gpu_util import pack_workload
+from gpu_util import f64, pack_workload
 
 
-def _flat_ref(lib, y_routed, inv, T, k):
-    return lib.unpermute(y_routed, inv, None, T, k)
+def _flat_ref(y_routed, ids, E, T, k):
+    """The routed rows in flat order t*k + j, by the oracle's routing plan and
+    combine."""
+    _, _, inv_r = oracle.route(ids, E)
+    return oracle.unpermute(f64(y_routed), inv_r, None, T, k)
 
 
 @pytest.mark.gpu
@@ -31,11 +37,11 @@ def test_gather_flat_matches_unpermute(lib, name, swiglu, paired):
     epi = lib.EPI_SWIGLU if swiglu else lib.EPI_NONE
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
     y = lib.grouped_spgemm_gather(x, perm, wl.k, off, w, epi)
-    ref = _flat_ref(lib, y, inv, wl.T, wl.k)
-    flat = torch.full_like(ref, 7)   # every row must be overwritten
+    ref = _flat_ref(y, ids, wl.E, wl.T, wl.k)
+    flat = torch.full_like(y, 7)   # every row must be overwritten
     lib.grouped_spgemm_gather(x, perm, wl.k, off, w, epi | lib.OUT_FLAT, out=flat)
     torch.cuda.synchronize()
-    assert torch.equal(flat, ref), name
+    assert np.array_equal(f64(flat), ref), name
 
 
 @pytest.mark.gpu
@@ -52,13 +58,13 @@ def test_fused_route_flat_matches_unpermute(lib, name, swiglu, paired):
     epi = lib.EPI_SWIGLU if swiglu else lib.EPI_NONE
     ids_d = torch.from_numpy(ids).cuda()
     y, off, perm, inv = lib.route_grouped_spgemm(ids_d, x, wl.k, w, epi)
-    ref = _flat_ref(lib, y, inv, wl.T, wl.k)
-    flat = torch.full_like(ref, 7)
+    ref = _flat_ref(y, ids, wl.E, wl.T, wl.k)
+    flat = torch.full_like(y, 7)
     _, off2, perm2, inv2 = lib.route_grouped_spgemm(ids_d, x, wl.k, w, epi | lib.OUT_FLAT,
                                                     out=flat)
     torch.cuda.synchronize()
     assert torch.equal(off2, off) and torch.equal(perm2, perm) and torch.equal(inv2, inv)
-    assert torch.equal(flat, ref), name
+    assert np.array_equal(f64(flat), ref), name
 
 
 @pytest.mark.gpu
@@ -71,15 +77,15 @@ def test_flat_with_invalid_routing_entries(lib):
     x = synth.tokens(wl).cuda()
     off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
     y = lib.grouped_spgemm_gather(x, perm, wl.k, off, w, lib.EPI_NONE)
-    ref = _flat_ref(lib, y, inv, wl.T, wl.k)
+    ref = torch.from_numpy(_flat_ref(y, ids, wl.E, wl.T, wl.k)).cuda()
     bad = perm.clone()
     lost = [3, 40, wl.M - 1]                      # routed rows given invalid entries
     gone = perm[lost].long()                      # their flat rows, now written by nobody
     bad[lost] = torch.tensor([-1, wl.M, 1 << 20], dtype=torch.int32, device=bad.device)
-    flat = torch.full_like(ref, 7)
+    flat = torch.full_like(y, 7)
     lib.grouped_spgemm_gather(x, bad, wl.k, off, w, lib.EPI_NONE | lib.OUT_FLAT, out=flat)
     torch.cuda.synchronize()
     keep = torch.ones(wl.M, dtype=torch.bool, device=flat.device)
     keep[gone] = False
-    assert torch.equal(flat[keep], ref[keep])
+    assert torch.equal(flat[keep].double(), ref[keep])
     assert bool((flat[~keep] == 7).all())

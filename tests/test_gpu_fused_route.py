@@ -67,16 +67,21 @@ def test_fused_fallback_and_empty(lib):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("paired", [False, True])
-def test_fused_against_oracle(lib, paired):
+@pytest.mark.parametrize("paired,tiled", [(False, False), (False, True), (True, True)])
+def test_fused_against_oracle(lib, paired, tiled):
     """A decode batch (E=16, T=8, k=2, N=64, K=256) routed in the GEMM launch,
-    against the float64 oracle."""
+    and the same batch through the gather GEMM, against the float64 oracle;
+    4:8 weights in the canonical and the tiled layout, paired weights tiled
+    (the canonical paired layout is an exchange format the GEMM rejects)."""
     wl = synth.Workload("fused", E=16, T=8, k=2, proj=(("w", 64, 256),), outliers=True,
                         bias="gauss", seed=4242)
     ids, _ = synth.routing(wl)
     x = synth.tokens(wl)
-    w = lib.tile_weights(pack_workload(lib, wl, 0, paired=paired))
+    w = pack_workload(lib, wl, 0, paired=paired)
+    if tiled:
+        w = lib.tile_weights(w)
     y, off, perm, inv = lib.route_grouped_spgemm(torch.from_numpy(ids).cuda(), x.cuda(), wl.k, w)
+    yg = lib.grouped_spgemm_gather(x.cuda(), perm, wl.k, off, w)
     torch.cuda.synchronize()
     off_r, perm_r, inv_r = oracle.route(ids, wl.E)
     assert np.array_equal(off.cpu().numpy(), off_r)
@@ -85,7 +90,28 @@ def test_fused_against_oracle(lib, paired):
     dec = [oracle_decode(oracle_expert(wl, 0, e, paired=paired)) for e in range(wl.E)]
     y_ref = oracle.grouped_gemm(oracle.permute(x.to(torch.float64).numpy(), perm_r, wl.k), off_r,
                                 lambda e: dec[e])
-    tol_check(f64(y), y_ref, f"fused decode batch, paired={paired}")
+    tol_check(f64(y), y_ref, f"fused decode batch, paired={paired}, tiled={tiled}")
+    tol_check(f64(yg), y_ref, f"gather GEMM, paired={paired}, tiled={tiled}")
+
+
+@pytest.mark.gpu
+def test_gather_canonical_prefill_against_oracle(lib):
+    """The gather GEMM on canonical (untiled) 4:8 weights over a batch with
+    more than 32 rows per expert on average (the contraction tile), with
+    SwiGLU, against the oracle."""
+    wl = synth.Workload("gather-canonical", E=4, T=96, k=2, proj=(("w", 128, 320),),
+                        outliers=True, bias="gauss", seed=4343)
+    ids, _ = synth.routing(wl)
+    x = synth.tokens(wl)
+    w = pack_workload(lib, wl, 0)
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    y = lib.grouped_spgemm_gather(x.cuda(), perm, wl.k, off, w, lib.EPI_SWIGLU)
+    torch.cuda.synchronize()
+    off_r, perm_r, _ = oracle.route(ids, wl.E)
+    dec = [oracle_decode(oracle_expert(wl, 0, e)) for e in range(wl.E)]
+    y_ref = oracle.grouped_gemm(oracle.permute(x.to(torch.float64).numpy(), perm_r, wl.k), off_r,
+                                lambda e: dec[e])
+    tol_check(f64(y), oracle.bf16_round(oracle.swiglu(y_ref)), "gather GEMM, canonical, SwiGLU")
 
 
 @pytest.mark.gpu

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (assert_same_pack, f64, oracle_decode, oracle_expert, pack_workload,
-                      tol_check)
+from gpu_util import (assert_same_pack, f64, oracle_decode, oracle_expert, oracle_experts,
+                      pack_workload, pick_experts, tol_check)
 
 pytestmark = pytest.mark.gpu
 
@@ -166,10 +166,10 @@ def _paired_case(lib, loads, N, K, swiglu, seed):
     ([40] * 4, 64, 64, False),                             # K below one chunk
     ([300, 260], 576, 512, True),                          # 32-row tile, SwiGLU
     ([0, 3, 0, 1], 32, 64, False),
-    # tile choice: M = 4E one launch of the one-fragment streaming tile (an
-    # expert of 20 rows takes two token tiles); above, experts of up to 32
-    # rows on the two-fragment streaming tile and larger ones on the
-    # contraction tile, in two launches
+    # tile choice of a short call (one launch): M = 4E the one-fragment
+    # streaming tile (an expert of 20 rows takes two token tiles); up to 32
+    # rows per expert on average the two-fragment streaming tile, above it
+    # the contraction tile
     ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, True),
     ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, False),
     ([80, 0, 40, 8], 128, 512, True),
@@ -223,19 +223,12 @@ def test_paired_gather_matches_permute(lib, name, swiglu):
     assert not got[[0, wl.M - 1]].any()
 
 
-def _sample(counts, rng, n_random=2):
-    active = np.nonzero(counts)[0]
-    pick = {int(active[np.argmax(counts[active])]), int(active[np.argmin(counts[active])])}
-    for e in rng.choice(active, size=min(n_random, len(active)), replace=False):
-        pick.add(int(e))
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["decode-30b", "prefill-30b", "decode-1t", "prefill-1t"])
 def test_paired_workloads(lib, name):
     """Full-size workloads with paired weights: gate/up (SwiGLU on the
-    trillion-class chain) and, for the chain, the down projection; sampled
-    experts against the oracle (packed bytes, up to 128 rows each)."""
+    trillion-class chain) and, for the chain, the down projection.  Sampled
+    experts (the largest, one from each launch range of row counts, a random
+    one) against the oracle: packed bytes and every routed row."""
     wl = synth.WORKLOADS[name]
     ids, _ = synth.routing(wl)
     x = synth.tokens(wl)
@@ -246,6 +239,7 @@ def test_paired_workloads(lib, name):
     epi = lib.EPI_SWIGLU if wl.swiglu else lib.EPI_NONE
     y1 = lib.grouped_spgemm_gather(x.cuda(), perm, wl.k, off, w1t, epi)
     y2 = None
+    w2 = None
     if len(wl.proj) > 1:
         w2 = pack_workload(lib, wl, 1, paired=True)
         y2 = lib.grouped_spgemm(y1, off, lib.tile_weights(w2))
@@ -254,19 +248,20 @@ def test_paired_workloads(lib, name):
     counts = np.diff(off_r)
     x64 = x.to(torch.float64).numpy()
     rng = np.random.default_rng(wl.seed + 5)
-    for e in _sample(counts, rng):
-        p1 = oracle_expert(wl, 0, e, paired=True)
-        assert_same_pack(w1, e, p1, f"{name} expert {e}")
+    picks = pick_experts(counts, rng)
+    say(f"[{name}] oracle for experts {picks} (rows {[int(counts[e]) for e in picks]})")
+    ref1 = oracle_experts(wl, 0, picks, paired=True)
+    ref2 = oracle_experts(wl, 1, picks, paired=True) if y2 is not None else None
+    for e in picks:
+        assert_same_pack(w1, e, ref1[e][0], f"{name} expert {e}")
         rows = np.arange(off_r[e], off_r[e + 1])
-        if len(rows) > 128:
-            rows = np.concatenate([rows[:64], rows[-64:]])
-        ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], oracle_decode(p1))
+        ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], ref1[e][1])
         if wl.swiglu:
             ref = oracle.bf16_round(oracle.swiglu(ref))
         sel = torch.from_numpy(rows).cuda()
         tol_check(f64(y1[sel]), ref, f"{name} expert {e} ({counts[e]} rows)")
         if y2 is not None:
-            p2 = oracle_expert(wl, 1, e, paired=True)
-            ref2 = oracle.expert_gemm(f64(y1[sel]), oracle_decode(p2))
-            tol_check(f64(y2[sel]), ref2, f"{name} down expert {e}")
+            assert_same_pack(w2, e, ref2[e][0], f"{name} down expert {e}")
+            # the down GEMM from the oracle's own h, as the chain defines it
+            tol_check(f64(y2[sel]), oracle.expert_gemm(ref, ref2[e][1]), f"{name} down expert {e}")
         say(f"[{name}] expert {e}: {counts[e]} rows ok")

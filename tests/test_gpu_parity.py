@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (assert_same_pack, f64, oracle_expert, pack_workload, tol_check)
+from gpu_util import (assert_same_pack, f64, oracle_expert, oracle_experts, pack_workload,
+                      pick_experts, tol_check)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,22 +32,6 @@ def _gpu_route(m, ids_np, E, k):
     off, perm, inv = m.route(ids, E, k)
     torch.cuda.synchronize()
     return off.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy()
-
-
-def _pick(counts, rng, n_random=2):
-    """Experts to sample: the largest, a tiny one (< 16 rows), a mid one, and
-    a few random active experts."""
-    active = np.nonzero(counts)[0]
-    pick = {int(active[np.argmax(counts[active])])}
-    small = active[counts[active] < 16]
-    if len(small):
-        pick.add(int(small[0]))
-    mid = active[(counts[active] >= 16) & (counts[active] <= 200)]
-    if len(mid):
-        pick.add(int(mid[len(mid) // 2]))
-    for e in rng.choice(active, size=min(n_random, len(active)), replace=False):
-        pick.add(int(e))
-    return sorted(pick)
 
 
 # ------------------------------------------------------------------ packing
@@ -305,10 +290,10 @@ def test_spgemm_edges(lib, loads, N, K, swiglu):
     ([5, 0, 64, 127, 128, 129, 1], 32, 448, False),
     ([1] * 20, 128, 256, True),
     ([40] * 4, 64, 64, False),
-    # tile choice: M = 4E one launch of the one-fragment streaming tile (an
-    # expert of 20 rows takes two token tiles); above, experts of up to 32
-    # rows on the two-fragment streaming tile and larger ones on the
-    # contraction tile, in two launches
+    # tile choice of a short call (one launch): M = 4E the one-fragment
+    # streaming tile (an expert of 20 rows takes two token tiles); up to 32
+    # rows per expert on average the two-fragment streaming tile, above it
+    # the contraction tile
     ([20, 0, 10, 2, 0, 0, 0, 0], 64, 512, False),
     ([20, 1, 10, 2, 0, 0, 0, 0], 64, 512, True),
     ([80, 0, 40, 8], 128, 512, False),
@@ -344,44 +329,57 @@ def test_spgemm_gather_matches_permute(lib, name, swiglu):
     assert not got[[0, wl.M // 2, wl.M - 1]].any()
 
 
-@pytest.mark.parametrize("name", ["decode-30b", "prefill-30b"])
-def test_spgemm_30b_workloads(lib, name):
-    """Full-size 30B-class workloads; sampled experts are checked against the
-    oracle: their packed bytes and every routed row (up to 256 per expert)."""
-    wl = synth.WORKLOADS[name]
-    _, N, K = wl.proj[0]
-    ids, _ = synth.routing(wl)
-    x = synth.tokens(wl)
-    say(f"[{name}] packing {wl.E} experts on the GPU")
-    w = pack_workload(lib, wl, 0)
-    wt = lib.tile_weights(w)
-    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
-    xr = lib.permute(x.cuda(), perm, wl.k)
-    say(f"[{name}] grouped GEMM M={wl.M} N={N} K={K} (tiled weights)")
-    y = lib.grouped_spgemm(xr, off, wt)
+def _split_launch_case(lib, paired, swiglu):
+    """A call of at least 5.5e11 multiply-adds: the library splits the experts
+    over three launches by their own row counts (up to 16, 17-32, more).
+    Experts of 9, 16, 17, 25, 32, 33 and 65,468 rows cover every launch and
+    both sides of each boundary; every row of the small experts and 256 rows
+    of the large one are checked against the oracle."""
+    loads = [9, 16, 17, 25, 32, 33, 65468]
+    N, K = 2048, 4096
+    M = sum(loads)
+    assert M * N * K >= 5.5e11
+    E = len(loads)
+    ids = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(loads)])
+    ids = ids[np.random.default_rng(77).permutation(M)]
+    wl = synth.Workload("split", E=E, T=M, k=1, proj=(("w", N, K),), outliers=True,
+                        bias="none", seed=4242)
+    x = synth.tokens(wl, T=M, K=K)
+    say(f"[split launches] paired={paired} swiglu={swiglu}: packing {E} experts {N}x{K}")
+    w = lib.tile_weights(pack_workload(lib, wl, 0, paired=paired))
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), E, 1)
+    y = lib.grouped_spgemm_gather(x.cuda(), perm, 1, off, w,
+                                  lib.EPI_SWIGLU if swiglu else lib.EPI_NONE)
     torch.cuda.synchronize()
-    off_r, perm_r, _ = oracle.route(ids, wl.E)
-    counts = np.diff(off_r)
+    off_r, perm_r, _ = oracle.route(ids, E)
     x64 = x.to(torch.float64).numpy()
-    rng = np.random.default_rng(wl.seed)
-    for e in _pick(counts, rng):
-        p = oracle_expert(wl, 0, e)
-        assert_same_pack(w, e, p, f"{name} expert {e}")
+    ref = oracle_experts(wl, 0, range(E), paired=paired)
+    for e in range(E):
         rows = np.arange(off_r[e], off_r[e + 1])
         if len(rows) > 256:
             rows = np.concatenate([rows[:128], rows[-128:]])
-        ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], oracle.decode(p))
-        tol_check(f64(y[torch.from_numpy(rows).cuda()]), ref, f"{name} expert {e} ({counts[e]} rows)")
-        say(f"[{name}] expert {e}: {counts[e]} rows ok")
+        want = oracle.expert_gemm(x64[perm_r[rows]], ref[e][1])
+        if swiglu:
+            want = oracle.bf16_round(oracle.swiglu(want))
+        tol_check(f64(y[torch.from_numpy(rows).cuda()]), want,
+                  f"split launches paired={paired} swiglu={swiglu} expert {e} ({loads[e]} rows)")
+    say(f"[split launches] paired={paired} swiglu={swiglu} ok")
+
+
+@pytest.mark.parametrize("paired,swiglu", [(False, False), (False, True), (True, False),
+                                           (True, True)])
+def test_spgemm_split_launches(lib, paired, swiglu):
+    _split_launch_case(lib, paired, swiglu)
 
 
 @pytest.mark.parametrize("name", ["decode-1t", "prefill-1t"])
 def test_chain_1t_workloads(lib, name):
-    """Full-size trillion-class chain: permute -> gate/up GEMM with SwiGLU ->
-    down GEMM -> combine.  Sampled experts: packed bytes, h rows and Y2 rows
-    against the oracle chain; the weighted combine at full size against the
-    weighted sum of the device's own Y2 rows (a property that holds at any
-    size)."""
+    """Full-size trillion-class chain in the benchmark's launch configuration:
+    dispatch fused into the gate/up GEMM with SwiGLU -> down GEMM -> combine.
+    Sampled experts (the largest, one from each launch range of row counts
+    and a random one): packed bytes and every h and Y2 row against the oracle
+    chain.  The combine at full size against the oracle's combine of the
+    device's Y2 (float64 on the host)."""
     wl = synth.WORKLOADS[name]
     ids, tw = synth.routing(wl)
     x = synth.tokens(wl)
@@ -400,28 +398,25 @@ def test_chain_1t_workloads(lib, name):
     counts = np.diff(off_r)
     x64 = x.to(torch.float64).numpy()
     rng = np.random.default_rng(wl.seed)
-    for e in _pick(counts, rng, n_random=1):
-        p1 = oracle_expert(wl, 0, e)
-        p2 = oracle_expert(wl, 1, e)
-        assert_same_pack(w1, e, p1, f"{name} gate_up expert {e}")
-        assert_same_pack(w2, e, p2, f"{name} down expert {e}")
+    picks = pick_experts(counts, rng)
+    say(f"[{name}] oracle for experts {picks} (rows {[int(counts[e]) for e in picks]})")
+    ref1 = oracle_experts(wl, 0, picks)
+    ref2 = oracle_experts(wl, 1, picks)
+    for e in picks:
+        assert_same_pack(w1, e, ref1[e][0], f"{name} gate_up expert {e}")
+        assert_same_pack(w2, e, ref2[e][0], f"{name} down expert {e}")
         rows = np.arange(off_r[e], off_r[e + 1])
-        if len(rows) > 128:
-            rows = np.concatenate([rows[:64], rows[-64:]])
-        y1_ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], oracle.decode(p1))
+        y1_ref = oracle.expert_gemm(x64[perm_r[rows] // wl.k], ref1[e][1])
         h_ref = oracle.bf16_round(oracle.swiglu(y1_ref))
-        y2_ref = oracle.expert_gemm(h_ref, oracle.decode(p2))
+        y2_ref = oracle.expert_gemm(h_ref, ref2[e][1])
         rows_t = torch.from_numpy(rows).cuda()
         tol_check(f64(h[rows_t]), h_ref, f"{name} h, expert {e}")
         tol_check(f64(y2[rows_t]), y2_ref, f"{name} Y2, expert {e}")
         say(f"[{name}] expert {e}: {counts[e]} rows ok")
+    y2_host = f64(y2)
+    want = oracle.unpermute(y2_host, inv_r, tw if wl.weighted_combine else None, wl.T, wl.k)
     if wl.weighted_combine:
-        # computed by torch in float64 on the device, from the device's own Y2
-        invr = torch.from_numpy(inv_r.reshape(wl.T, wl.k).astype(np.int64)).cuda()
-        twr = tw_d.reshape(wl.T, wl.k).double()
-        want = torch.zeros(wl.T, y2.shape[1], dtype=torch.float64, device="cuda")
-        for j in range(wl.k):
-            want += twr[:, j:j + 1] * y2[invr[:, j]].double()
-        tol_check(f64(out), f64(want), f"{name} weighted combine")
+        tol_check(f64(out), want, f"{name} weighted combine")
     else:
-        assert torch.equal(out, y2[torch.from_numpy(inv_r.astype(np.int64)).cuda()])
+        assert np.array_equal(f64(out), want)
+    say(f"[{name}] combine ok")

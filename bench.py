@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain gather copy of known size (moesq_unpermute without "
                          "weights over 512 MiB in, 512 MiB out) to scale HBM byte counters")
+    ap.add_argument("--record-counters", metavar="DIR",
+                    help="no GPU: read the rocprofv3 counter CSVs under DIR (DIR/<case>/<pass>/..., "
+                         "case = a workload name, <workload>_paired, or calibrate) and write "
+                         "profiles/spgemm_counters.json")
     return ap.parse_args()
 
 
@@ -321,22 +325,116 @@ def sweep(m, wl, Gs=(1, 4, 16, 64, 128, 384), Rs=(1, 2, 4, 8, 16, 32, 64), launc
             del g
 
 
-def measured_traffic(workload, proj_name, paired=False):
-    """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
-    counter summary, or None when the GEMM source has changed since the
-    counters were taken (or no summary covers this workload)."""
-    path = os.path.join(ROOT, "profiles", "spgemm_counters.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except OSError:
-        return None
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "spgemm_counters.json")
+COPY_BYTES = 65536 * 4096 * 2          # calibrate_copy: bytes read and bytes written
+
+
+def gemm_source_sha():
+    """Hash of the GEMM's sources: counters taken on other sources are stale."""
     csrc = os.path.join(ROOT, "sparse_fp4_expert_amd", "csrc")
     src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in ("spgemm.hip", "common.hpp"))
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    return hashlib.sha256(src).hexdigest()
+
+
+def measured_counters(workload, proj_name, paired=False):
+    """Per-call counter figures of the grouped GEMM from the committed
+    rocprofv3 summary (traffic_bytes, mfma_flops, ...), or {} when the GEMM
+    source has changed since the counters were taken (or no summary covers
+    this workload)."""
+    try:
+        with open(COUNTERS_JSON) as f:
+            rec = json.load(f)
+    except OSError:
+        return {}
+    if gemm_source_sha() != rec.get("source_sha256"):
+        return {}
+    return rec.get("kernels", {}).get(f"{workload}/{proj_name}" + ("/paired" if paired else ""), {})
+
+
+def _kernel_tile(name):
+    """(MS, SWIGLU) of a grouped-GEMM kernel from its demangled name, or None."""
+    import re
+    m = re.search(r"spgemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (\d+)", name)
+    if not m:
         return None
-    k = rec.get("kernels", {}).get(f"{workload}/{proj_name}" + ("/paired" if paired else ""))
-    return None if k is None else k.get("traffic_bytes")
+    return int(m.group(2)), m.group(6) == "true"
+
+
+def record_counters(root):
+    """Turns rocprofv3 counter CSVs into profiles/spgemm_counters.json.
+
+    Layout: root/<case>/<pass>/.../*counter_collection.csv with case a
+    workload name, <workload>_paired, or calibrate (bench.py
+    --calibrate-copy).  Per kernel: the mean over its dispatches of each
+    counter; per GEMM call: the sum over the kernels of that projection (one
+    to three launches).  HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB) times
+    the factor that makes the calibration copy read and write its known
+    512 MiB; executed MFMA flops = SQ_INSTS_MFMA (wave instructions) times
+    the multiply-adds of one instruction x 2 (32x32x16 and the sparse
+    32x32x32: 32768; 16x16x32 and the sparse 16x16x64: 16384)."""
+    import csv
+    import glob
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))   # case -> kernel -> (dispatch, counter)
+    for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        case = os.path.relpath(path, root).split(os.sep)[0]
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                key = (row.get("Dispatch_Id") or row.get("Correlation_Id"), row["Counter_Name"])
+                per[case][row["Kernel_Name"]][key] += float(row["Counter_Value"])
+
+    def means(kernel_rows):
+        by = defaultdict(list)
+        for (_, ctr), v in kernel_rows.items():
+            by[ctr].append(v)
+        return {c: sum(v) / len(v) for c, v in by.items()}
+
+    cal = {}
+    for name, rows in per.get("calibrate", {}).items():
+        if "unpermute" in name:
+            cal = means(rows)
+    if "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
+        raise SystemExit("record-counters: the calibrate case needs FETCH_SIZE and WRITE_SIZE of the copy")
+    ff = COPY_BYTES / 1024 / cal["FETCH_SIZE"]
+    wf = COPY_BYTES / 1024 / cal["WRITE_SIZE"]
+    about = ("Per call of the grouped GEMM (the sum over the one to three launches of the "
+             "call; each launch the mean over its dispatches): rocprofv3 counters; traffic_bytes "
+             "= FETCH_SIZE and WRITE_SIZE (KiB) scaled so that a gather copy of known size "
+             "(bench.py --calibrate-copy) reads and writes its 512 MiB; mfma_flops = "
+             "SQ_INSTS_MFMA x 2 x the multiply-adds one MFMA instruction executes.")
+    out = {"about": about,
+           "calibration": {"copy_bytes_each_way": COPY_BYTES, "fetch_size_kib": cal["FETCH_SIZE"],
+                           "fetch_factor": ff, "write_size_kib": cal["WRITE_SIZE"],
+                           "write_factor": wf},
+           "source_sha256": gemm_source_sha(), "kernels": {}}
+    for case, kernels in sorted(per.items()):
+        if case == "calibrate":
+            continue
+        paired = case.endswith("_paired")
+        wl = synth.WORKLOADS[case[:-len("_paired")] if paired else case]
+        for p, (pname, _, _) in enumerate(wl.proj):
+            acc = defaultdict(float)
+            names = []
+            for name, rows in kernels.items():
+                tile = _kernel_tile(name)
+                if tile is None or (len(wl.proj) > 1 and tile[1] != (p == 0)):
+                    continue
+                names.append(name)
+                m = means(rows)
+                for c, v in m.items():
+                    acc[c] += v
+                if "SQ_INSTS_MFMA" in m:
+                    acc["mfma_flops"] += m["SQ_INSTS_MFMA"] * (32768 if tile[0] == 32 else 16384)
+            if not names:
+                continue
+            rec = {"launches": len(names), "kernels": sorted(names)}
+            rec.update({c: round(v, 2) for c, v in acc.items()})
+            if "FETCH_SIZE" in acc and "WRITE_SIZE" in acc:
+                rec["traffic_bytes"] = acc["FETCH_SIZE"] * 1024 * ff + acc["WRITE_SIZE"] * 1024 * wf
+            out["kernels"][f"{wl.name}/{pname}" + ("/paired" if paired else "")] = rec
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {COUNTERS_JSON}: {sorted(out['kernels'])}")
 
 
 def gemm_work(wl, ids, paired=False):
@@ -443,6 +541,9 @@ def cpu_baseline(wl, budget_s, paired=False):
 
 def main():
     args = parse()
+    if args.record_counters:
+        record_counters(args.record_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               "(one process drives one GPU; expert sharding across GPUs is not built)", file=sys.stderr)
@@ -498,23 +599,22 @@ def main():
     g0 = f"gemm_{wl.proj[0][0]}"
     g0_ms = kernel_ms[g0]
     f0, b0 = work[0]
+    cnt = measured_counters(wl.name, wl.proj[0][0], args.paired)
     if prefill:
-        roof = {"bound": "mfma", "achieved": f0 / (g0_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-        # MFMAs the kernels execute: each expert's rows padded to whole token
-        # fragments, 32 rows on the contraction tile (experts of more than 32
-        # rows), 16 on the streaming tile (the others); one MAC per kept
-        # weight is the useful rate.  Paired weights run on the sparse MFMA,
-        # whose pipe retires twice the dense-equivalent work of the dense MFMA.
-        _, N0, K0 = wl.proj[0]
-        counts = np.bincount(step.ids_host, minlength=wl.E)
-        big = counts > 32
-        padded = float((-(-counts[big] // 32) * 32).sum() + (-(-counts[~big] // 16) * 16).sum())
-        pipe_peak = PEAK_BF16_TFLOPS * (2 if args.paired else 1)
-        roof["mfma_executed_tflops"] = 2.0 * padded * N0 * K0 / (g0_ms * 1e-3) / 1e12
-        roof["mfma_executed_frac"] = roof["mfma_executed_tflops"] / pipe_peak
-        roof["mfma_pipe_peak"] = pipe_peak
-        roof["useful_tflops"] = 0.5 * roof["achieved"]
+        # The method's own work: one multiply-add per kept weight (half of the
+        # N x K weights) per routed row, i.e. M*N*K flops per projection.
+        roof = {"bound": "mfma", "achieved": 0.5 * f0 / (g0_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "work": "useful: M*N*K flops (one multiply-add per kept weight and routed row)"}
+        roof["dense_equiv_tflops"] = f0 / (g0_ms * 1e-3) / 1e12
+        # MFMA work the kernels execute, from the committed rocprofv3
+        # SQ_INSTS_MFMA count of the same GEMM source (null when stale): it
+        # includes the zeros of the 4:8 groups that the dense MFMA multiplies
+        # and the padding of each expert's rows to whole fragments.
+        mf = cnt.get("mfma_flops")
+        roof["mfma_executed_tflops"] = None if mf is None else mf / (g0_ms * 1e-3) / 1e12
+        roof["mfma_executed_frac"] = (None if mf is None
+                                      else roof["mfma_executed_tflops"] / PEAK_BF16_TFLOPS)
     else:
         roof = {"bound": "hbm", "achieved": b0 / (g0_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -524,7 +624,7 @@ def main():
         roof["read_ceiling_gbs"] = ceil
         roof["frac_of_read_ceiling"] = roof["achieved"] / ceil
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name, wl.proj[0][0], args.paired)
+    roof["traffic"] = cnt.get("traffic_bytes")
     roof["kernel"] = f"moesq_grouped_spgemm ({wl.proj[0][0]})"
     roof["kernel_ms"] = g0_ms
 

@@ -187,6 +187,29 @@ moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_
 size_t moesq_route_workspace_bytes(int32_t T, int32_t k, int32_t E);
 
 /*
+ * moesq_route for callers that cannot allocate device memory: code under HIP
+ * graph capture that must not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and limits as moesq_route,
+ * bit for bit, without the workspace: when the ids need the block counts
+ * (moesq_route_workspace_bytes(T, k, E) > 0) they go to a scratch array of
+ * MOESQ_ROUTE_SCRATCH_BYTES that the library holds in device memory, one per
+ * device, from the device's first call until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *   Returns MOESQ_ERR_SHAPE, launching nothing, when the counts need more
+ *   than MOESQ_ROUTE_SCRATCH_BYTES (for example E = 384 above about 1.4
+ *   million ids, E = 1024 above 524,288 ids); moesq_route with a workspace
+ *   takes those.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (different streams, or graphs replayed
+ * concurrently) race and give unspecified plans.  The scratch needs no
+ * clearing: each call writes every count it reads.
+ */
+#define MOESQ_ROUTE_SCRATCH_BYTES ((size_t)4 << 20)
+moesq_status_t moesq_route_noalloc(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                                   int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
+                                   hipStream_t stream);
+
+/*
  * Dispatch: x_routed[r][:] = x[perm[r] / k][:].
  *   x         [T][K] bf16;  perm [T*k] int32 (from moesq_route);
  *   x_routed  [T*k][K] bf16 out.  Rows with perm[r] outside [0, T*k) are zero.

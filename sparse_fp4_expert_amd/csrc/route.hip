@@ -21,6 +21,9 @@
 // into blocks of ROUTE_BLOCK_IDS: a histogram kernel per block, one scan
 // kernel over (block, expert) counts in the workspace, and a scatter kernel
 // per block.
+#include <mutex>
+#include <string>
+
 #include "common.hpp"
 #include "route_dev.hpp"
 
@@ -194,6 +197,37 @@ __global__ __launch_bounds__(RB_THREADS) void route_scatter_kernel(
 
 static long long route_blocks(long long M) { return (M + ROUTE_BLOCK_IDS - 1) / ROUTE_BLOCK_IDS; }
 
+// Scratch of moesq_route_noalloc: the per-block expert counts live in this
+// file-scope device array instead of a caller's workspace.  Each device that
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address): set-up takes each device's address once with
+// hipGetSymbolAddress and the launches use that.
+constexpr size_t ROUTE_SCRATCH_BYTES = MOESQ_ROUTE_SCRATCH_BYTES;
+static __device__ __align__(256) int scratch[ROUTE_SCRATCH_BYTES / sizeof(int)];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+
+// Address of this device's scratch, taken on the device's first call.
+static moesq_status_t scratch_ptr(int **out) {
+  static std::mutex mu;
+  static int *ptr[SCRATCH_MAX_DEVICES] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(MOESQ_ERR_HIP, "moesq_route_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOESQ_ERR_HIP, std::string("moesq_route_noalloc: hipGetSymbolAddress: ") +
+                                     hipGetErrorString(e));
+    ptr[dev] = static_cast<int *>(p);
+  }
+  *out = ptr[dev];
+  return MOESQ_OK;
+}
+
 }  // namespace moesq
 
 using namespace moesq;
@@ -207,34 +241,74 @@ extern "C" size_t moesq_route_workspace_bytes(int32_t T, int32_t k, int32_t E) {
   return (size_t)(route_blocks(M) * E * sizeof(int));
 }
 
+// Host checks shared by both routing entry points.
+static moesq_status_t route_check(const char *who, const int32_t *topk_ids, int32_t T, int32_t k,
+                                  int32_t E, const int32_t *expert_offsets, const int32_t *perm,
+                                  const int32_t *inv_perm) {
+  const std::string w(who);
+  if (E < 1 || E > MOESQ_MAX_EXPERTS)
+    return fail(MOESQ_ERR_SHAPE, w + ": E must be in [1, " + std::to_string(MOESQ_MAX_EXPERTS) + "]");
+  if (k < 1 || k > E) return fail(MOESQ_ERR_SHAPE, w + ": k must be in [1, E]");
+  if (T < 0) return fail(MOESQ_ERR_SHAPE, w + ": T must be >= 0");
+  if ((long long)T * k >= (1ll << 31)) return fail(MOESQ_ERR_SHAPE, w + ": T*k must be < 2^31");
+  if (!expert_offsets) return fail(MOESQ_ERR_NULL, w + ": expert_offsets is NULL");
+  if ((long long)T * k > 0 && (!topk_ids || !perm || !inv_perm))
+    return fail(MOESQ_ERR_NULL, w + ": topk_ids, perm and inv_perm must be non-NULL");
+  return MOESQ_OK;
+}
+
+// The routing launches: one workgroup without counts, else the three
+// block kernels over `counts` (route_blocks(M) x E ints).
+static moesq_status_t route_launch(const char *who, const int32_t *topk_ids, int M, int E,
+                                   int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
+                                   int *counts, hipStream_t stream) {
+  if (!counts) {
+    // one workgroup: no workspace needed (slower for large inputs)
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, topk_ids, M, E,
+                       expert_offsets, perm, inv_perm);
+    return launch_status(who);
+  }
+  const int nb = (int)route_blocks(M);
+  hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids, M, E,
+                     counts);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, counts, nb, E,
+                     expert_offsets);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids, M, E,
+                     counts, expert_offsets, perm, inv_perm);
+  return launch_status(who);
+}
+
 extern "C" moesq_status_t moesq_route(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                                       int32_t *expert_offsets, int32_t *perm, int32_t *inv_perm,
                                       void *ws, size_t ws_bytes, hipStream_t stream) {
   clear_error();
-  if (E < 1 || E > MOESQ_MAX_EXPERTS)
-    return fail(MOESQ_ERR_SHAPE, "moesq_route: E must be in [1, " +
-                                     std::to_string(MOESQ_MAX_EXPERTS) + "]");
-  if (k < 1 || k > E) return fail(MOESQ_ERR_SHAPE, "moesq_route: k must be in [1, E]");
-  if (T < 0) return fail(MOESQ_ERR_SHAPE, "moesq_route: T must be >= 0");
-  const long long M = (long long)T * k;
-  if (M >= (1ll << 31)) return fail(MOESQ_ERR_SHAPE, "moesq_route: T*k must be < 2^31");
-  if (!expert_offsets) return fail(MOESQ_ERR_NULL, "moesq_route: expert_offsets is NULL");
-  if (M > 0 && (!topk_ids || !perm || !inv_perm))
-    return fail(MOESQ_ERR_NULL, "moesq_route: topk_ids, perm and inv_perm must be non-NULL");
+  moesq_status_t st =
+      route_check("moesq_route", topk_ids, T, k, E, expert_offsets, perm, inv_perm);
+  if (st != MOESQ_OK) return st;
   const size_t need = moesq_route_workspace_bytes(T, k, E);
-  if (need == 0 || !ws || ws_bytes < need) {
-    // one workgroup: no workspace needed (slower for large inputs)
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, topk_ids, (int)M, E,
-                       expert_offsets, perm, inv_perm);
-    return launch_status("moesq_route");
+  int *counts = (need == 0 || !ws || ws_bytes < need) ? nullptr : static_cast<int *>(ws);
+  return route_launch("moesq_route", topk_ids, T * k, E, expert_offsets, perm, inv_perm, counts,
+                      stream);
+}
+
+extern "C" moesq_status_t moesq_route_noalloc(const int32_t *topk_ids, int32_t T, int32_t k,
+                                              int32_t E, int32_t *expert_offsets, int32_t *perm,
+                                              int32_t *inv_perm, hipStream_t stream) {
+  static const char *who = "moesq_route_noalloc";
+  clear_error();
+  moesq_status_t st = route_check(who, topk_ids, T, k, E, expert_offsets, perm, inv_perm);
+  if (st != MOESQ_OK) return st;
+  const size_t need = moesq_route_workspace_bytes(T, k, E);
+  if (need > ROUTE_SCRATCH_BYTES)
+    return fail(MOESQ_ERR_SHAPE, std::string(who) + ": the block counts need " +
+                                     std::to_string(need) + " bytes, more than the " +
+                                     std::to_string(ROUTE_SCRATCH_BYTES) +
+                                     " bytes of the library's scratch; "
+                                     "use moesq_route with a workspace");
+  int *counts = nullptr;
+  if (need > 0) {
+    st = scratch_ptr(&counts);
+    if (st != MOESQ_OK) return st;
   }
-  const int nb = (int)route_blocks(M);
-  int *counts = static_cast<int *>(ws);
-  hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids, (int)M,
-                     E, counts);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(ROUTE_THREADS), 0, stream, counts, nb, E,
-                     expert_offsets);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(RB_THREADS), 0, stream, topk_ids,
-                     (int)M, E, counts, expert_offsets, perm, inv_perm);
-  return launch_status("moesq_route");
+  return route_launch(who, topk_ids, T * k, E, expert_offsets, perm, inv_perm, counts, stream);
 }

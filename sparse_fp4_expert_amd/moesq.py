@@ -49,6 +49,7 @@ def _sig(name, restype, *argtypes):
 
 _route = _sig("moesq_route", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp)
 _route_ws = _sig("moesq_route_workspace_bytes", _sz, _i32, _i32, _i32)
+_route_noalloc = _sig("moesq_route_noalloc", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _permute = _sig("moesq_permute", _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _spgemm = _sig("moesq_grouped_spgemm", _i32, _vp, _vp, _i32, ctypes.POINTER(WeightsDesc), _i32,
                _vp, _vp, _sz, _vp)
@@ -70,7 +71,8 @@ _status_string = _sig("moesq_status_string", ctypes.c_char_p, _i32)
 _last_error = _sig("moesq_last_error", ctypes.c_char_p)
 _version = _sig("moesq_version", _i32)
 
-EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_permute",
+EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_route_noalloc",
+            "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes",
             "moesq_grouped_spgemm_gather", "moesq_route_grouped_spgemm", "moesq_unpermute",
             "moesq_pack_weights", "moesq_pack_weights_paired", "moesq_tile_weights",
@@ -197,6 +199,22 @@ def moesq_route(topk_ids, T: int, k: int, E: int, expert_offsets, perm, inv_perm
 
 def moesq_route_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(_route_ws(T, k, E))
+
+
+ROUTE_SCRATCH_BYTES = 4 << 20
+
+
+def moesq_route_noalloc(topk_ids, T: int, k: int, E: int, expert_offsets, perm, inv_perm,
+                        stream=None):
+    """moesq_route without a workspace: the block counts go to the library's
+    own device scratch (ROUTE_SCRATCH_BYTES per device; calls that overlap on
+    one device race)."""
+    _sizes((topk_ids, T * k, "topk_ids"), (expert_offsets, E + 1, "expert_offsets"),
+           (perm, T * k, "perm"), (inv_perm, T * k, "inv_perm"))
+    _check(_route_noalloc(_ptr(topk_ids, torch.int32, "topk_ids"), T, k, E,
+                          _ptr(expert_offsets, torch.int32, "expert_offsets"),
+                          _ptr(perm, torch.int32, "perm"), _ptr(inv_perm, torch.int32, "inv_perm"),
+                          _stream(stream)))
 
 
 def moesq_permute(x, perm, T: int, k: int, K: int, x_routed, stream=None):

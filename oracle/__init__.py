@@ -33,6 +33,8 @@ from .paired import (PAIRS, PackedPairedExpert, decode_paired, paired_pattern,
 from .route import route
 from .moe import (grouped_gemm, moe_chain, permute, silu, swiglu, unpermute,
                   expert_gemm)
+from .w4a4 import (PackedActivations, decode_activations, quantize_activations,
+                   w4a4_expert_gemm)
 
 READINGS = {
     "format": "unconstrained 4:8: any 4 of 8 kept, 8-bit mask per group "
@@ -54,4 +56,10 @@ READINGS = {
     "paired_support": "keep the two pairs with the largest fp32 |w_2i|+|w_2i+1|; "
                       "equal sums -> lower pair index",
     "paired_values": "kept values quantised exactly as the 4:8 format",
+    "act_blocks": "W4A4: activations quantized to E2M1 with one E4M3 scale per 32 "
+                  "consecutive K positions (the weights' scale blocks)",
+    "act_row_scale": "W4A4: one fp32 scale per activation row, g_t = amax_t/(6*448) "
+                     "(g_t = 1 when amax_t = 0); s = E4M3(amax_32/(6 g_t)), "
+                     "q = E2M1(x/(s g_t)), all in fp32 with ties to even",
+    "act_codes": "W4A4: two codes per byte, position 2i in the low nibble",
 }

@@ -546,9 +546,124 @@ def pin_paired_matches_48(O, seed=12):
     assert np.array_equal(pp.scales, p4.scales) and pp.g == p4.g
 
 
+
+# ---------------------------------------------------------------- W4A4 activations
+
+def pin_act_fixture(O):
+    """The hand-derived NVFP4 quantization of two activation rows
+    (tests/golden/act_rows.txt): codes, scales, row scales and decoded values."""
+    d = {ln[0]: ln[1:] for ln in _lines("act_rows.txt")}
+    x = np.array([[float(v) for v in d["x0"]], [float(v) for v in d["x1"]]], np.float32)
+    p = O.quantize_activations(x)
+    assert p.g.tolist() == [float(v) for v in d["g"]], p.g
+    for r in range(2):
+        assert np.array_equal(p.scales[r], _hex(d[f"scales{r}"])), (r, p.scales[r])
+        assert np.array_equal(p.codes[r], _hex(d[f"codes{r}"])), (r, p.codes[r])
+        want = np.array([float(v) for v in d[f"decoded{r}"]])
+        assert np.array_equal(O.decode_activations(p)[r], want), r
+        assert np.array_equal(O.decode_activations(p, include_row_scale=False)[r],
+                              want / float(p.g[r])), r
+
+
+def _act_rows(rng, T=24, K=256):
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x *= np.exp(rng.uniform(-12, 12, (T, 1))).astype(np.float32)          # per-row range
+    x[:, rng.choice(K, 5, replace=False)] *= 10                            # outlier channels
+    x[3] = 0                                                               # zero row
+    x[4, 32:64] = 0                                                        # zero block
+    x[5, :] = np.float32(0.75) * np.sign(x[5])                             # all ties
+    x[6, 7] = -x[6].__abs__().max() * 2                                    # negative row max
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def pin_act_nearest(O, seed=14):
+    """On random bf16 rows: g is the fp32 amax/2688 (1 for a zero row); every
+    block scale is torch's float32 -> float8_e4m3fn cast of amax_b/(6g) below
+    448 and saturates to 448 above it; every code is a nearest E2M1 value of
+    x/(s g) (brute force over the grid, ties to the even code, saturation
+    at 6), with +0 for a zero result; zero rows and blocks decode to zero."""
+    rng = np.random.default_rng(seed)
+    x = _act_rows(rng)
+    p = O.quantize_activations(x)
+    T, K = x.shape
+    amax = np.abs(x).max(axis=1)
+    g = np.where(amax > 0, (amax / np.float32(2688)).astype(np.float32), np.float32(1))
+    assert np.array_equal(p.g, g.astype(np.float32))
+    six_g = (np.float32(6) * p.g).astype(np.float32)
+    ab = np.abs(x).reshape(T, K // 32, 32).max(axis=2)
+    r = (ab / six_g[:, None]).astype(np.float32)
+    lib = torch.from_numpy(np.minimum(r, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(p.scales, np.where(r >= 448, 0x7E, lib))
+    grid = np.float64([0, .5, 1, 1.5, 2, 3, 4, 6])
+    codes = np.empty((T, K), np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = p.codes & 15, p.codes >> 4
+    for t in range(T):
+        for b in range(K // 32):
+            sg = np.float32(np.float32(O.E4M3_VALUES[p.scales[t, b]]) * p.g[t])
+            for i in range(32):
+                c = int(codes[t, 32 * b + i])
+                v = O.E2M1_VALUES[c]
+                if sg == 0:
+                    assert c == 0
+                    continue
+                q = float(np.float32(np.float32(x[t, 32 * b + i]) / sg))
+                if abs(q) >= 6:
+                    assert v == np.sign(q) * 6, (t, b, i, q, c)
+                    continue
+                d = np.abs(abs(q) - grid)
+                best = np.flatnonzero(d == d.min())
+                assert abs(v) == grid[best[0] if len(best) == 1 else best[0] + (best[0] % 2)], (t, b, i, q, c)
+                assert (v == 0 and c == 0) or np.sign(v) == np.sign(q), (t, b, i, q, c)
+    dec = O.decode_activations(p)
+    assert not dec[3].any() and not dec[4, 32:64].any()
+
+
+def pin_act_invariances(O, seed=15):
+    """Rows are quantized on their own: permuting rows permutes the packed
+    rows; scaling a row by 2^p (within range) keeps its codes and scales and
+    scales g by 2^p; a row's largest magnitude decodes exactly (its block
+    scale is 448 and its code 6)."""
+    rng = np.random.default_rng(seed)
+    x = _act_rows(rng, T=16, K=128)
+    p = O.quantize_activations(x)
+    sigma = rng.permutation(16)
+    q = O.quantize_activations(x[sigma])
+    assert np.array_equal(q.codes, p.codes[sigma]) and np.array_equal(q.scales, p.scales[sigma])
+    assert np.array_equal(q.g, p.g[sigma])
+    s = O.quantize_activations(x * np.float32(2.0 ** 7))
+    nz = np.abs(x).max(axis=1) > 0
+    assert np.array_equal(s.codes, p.codes) and np.array_equal(s.scales, p.scales)
+    assert np.array_equal(s.g[nz], p.g[nz] * np.float32(2.0 ** 7))
+    dec = O.decode_activations(p)
+    for t in np.flatnonzero(nz):
+        k = int(np.argmax(np.abs(x[t])))
+        assert p.scales[t, k // 32] == 0x7E
+        assert abs(dec[t, k]) == abs(np.float64(x[t, k])) or abs(dec[t, k]) == 6 * 448 * float(p.g[t])
+
+
+def pin_w4a4_gemm_exact(O, seed=16):
+    """The W4A4 expert GEMM against exact rational arithmetic: its operands
+    are the dequantized activations (the pinned decode) and the dequantized
+    weights, both dyadic; the float64 result lies within gamma_K * sum |x||w|
+    of the exact sum."""
+    rng = np.random.default_rng(seed)
+    N, K, m = 5, 64, 8
+    W = O.decode(O.quantize((rng.standard_normal((N, K)) * 0.02).astype(np.float32)))
+    x = _act_rows(rng, T=m, K=K)
+    y = O.w4a4_expert_gemm(x, W)
+    xq = O.decode_activations(O.quantize_activations(x))
+    u = 2.0 ** -53
+    for r in range(m):
+        for n in range(N):
+            terms = [Fraction(float(xq[r, k])) * Fraction(float(W[n, k])) for k in range(K)]
+            mag = sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[r, n])) - sum(terms)) <= Fraction(K * u) * mag + Fraction(1, 2 ** 1074)
+
+
 ALL_PINS = [pin_e2m1_grid, pin_e4m3_table, pin_e4m3_encode, pin_e2m1_encode,
             pin_bf16_round, pin_quant_fixture, pin_support_bruteforce,
             pin_masks_and_layout, pin_quant_nearest, pin_route_bruteforce,
             pin_gemm_exact, pin_gemm_invariances, pin_unpermute, pin_swiglu,
             pin_paired_fixture, pin_paired_support_bruteforce, pin_paired_layout,
-            pin_paired_matches_48, pin_chain_fixture, pin_chain_bruteforce]
+            pin_paired_matches_48, pin_chain_fixture, pin_chain_bruteforce,
+            pin_act_fixture, pin_act_nearest, pin_act_invariances, pin_w4a4_gemm_exact]

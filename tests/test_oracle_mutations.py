@@ -231,3 +231,100 @@ def test_chain_silu_on_up_half():
         y2 = oracle.grouped_gemm(h, off, w_down)
         return y1, h, y2, oracle.unpermute(y2, inv, tw, x.shape[0], k)
     _chain_fails(_ns(moe_chain=chain))
+
+
+# ---------------------------------------------------------------- W4A4 activations
+
+import oracle.w4a4  # noqa: E402
+
+_ACT_PINS = (pins.pin_act_fixture, pins.pin_act_nearest)
+
+
+def _quant_act(x, g_of, block=32):
+    """The activation quantizer with the second-level scale from g_of(x) and
+    scale blocks of `block` positions (layout of 32-blocks kept)."""
+    x = np.asarray(x, np.float32)
+    T, K = x.shape
+    g = g_of(x)
+    six_g = (np.float32(6) * g).astype(np.float32)
+    ab = np.abs(x).reshape(T, K // block, block).max(axis=2)
+    sc = oracle.e4m3_encode((ab / six_g[:, None]).astype(np.float32))
+    sg = np.repeat((oracle.E4M3_VALUES[sc].astype(np.float32) * g[:, None]).astype(np.float32),
+                   block, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sg > 0, x / np.where(sg > 0, sg, 1), 0).astype(np.float32)
+    c = oracle.e2m1_encode(q)
+    step = 32 // block
+    return oracle.PackedActivations((c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8),
+                                    sc[:, ::step].astype(np.uint8), g.astype(np.float32))
+
+
+def test_act_per_tensor_scale():
+    # one second-level scale for the whole tensor instead of one per row
+    def g_tensor(x):
+        amax = np.float32(np.abs(x).max())
+        g = np.float32(amax / np.float32(2688)) if amax > 0 else np.float32(1)
+        return np.full(x.shape[0], g, np.float32)
+    _fails(pins.pin_act_fixture, _ns(quantize_activations=lambda x: _quant_act(x, g_tensor)))
+
+
+def _g_row(x):
+    amax = np.abs(x).max(axis=1)
+    return np.where(amax > 0, (amax / np.float32(2688)).astype(np.float32), np.float32(1))
+
+
+def test_act_blocks_of_16():
+    O = _ns(quantize_activations=lambda x: _quant_act(x, _g_row, block=16))
+    for pin in _ACT_PINS:
+        _fails(pin, O)
+
+
+def test_act_scale_without_six(monkeypatch):
+    monkeypatch.setattr(oracle.w4a4, "e4m3_encode",
+                        lambda v: oracle.formats.e4m3_encode(np.asarray(v) * 6))
+    for pin in _ACT_PINS:
+        _fails(pin, oracle)
+
+
+def test_act_nibbles_swapped():
+    real = oracle.quantize_activations
+
+    def q(x):
+        p = real(x)
+        p.codes = ((p.codes >> 4) | (p.codes << 4)).astype(np.uint8)
+        return p
+    O = _ns(quantize_activations=q)
+    for pin in _ACT_PINS:
+        _fails(pin, O)
+
+
+def test_act_decode_without_row_scale():
+    def dec(p, include_row_scale=True):
+        return oracle.decode_activations(p, include_row_scale=False)
+    _fails(pins.pin_act_fixture, _ns(decode_activations=dec))
+
+
+def test_act_scale_truncated(monkeypatch):
+    # block scales rounded down instead of to nearest
+    def trunc(v):
+        v = np.minimum(np.asarray(v, np.float64), 448)
+        pos = oracle.E4M3_VALUES[:0x7F]
+        return (np.searchsorted(pos, v, side="right") - 1).astype(np.uint8)
+    monkeypatch.setattr(oracle.w4a4, "e4m3_encode", trunc)
+    for pin in _ACT_PINS:
+        _fails(pin, oracle)
+
+
+def test_w4a4_gemm_unquantized_activations():
+    # the GEMM fed the bf16 activations instead of their NVFP4 rounding
+    def gemm(x_rows, W):
+        return np.asarray(x_rows, np.float64) @ np.asarray(W, np.float64).T
+    _fails(pins.pin_w4a4_gemm_exact, _ns(w4a4_expert_gemm=gemm))
+
+
+def test_act_mutation_harness_is_faithful():
+    # without a planted mistake the rewritten quantizer passes the pins, so
+    # the failures above come from the mistakes alone
+    O = _ns(quantize_activations=lambda x: _quant_act(x, _g_row))
+    for pin in _ACT_PINS:
+        pin(O)

@@ -52,6 +52,7 @@ import synth  # noqa: E402
 METRIC = "grouped sparse-FP4 GEMM TFLOP/s + weight GB/s (% of MFMA/HBM peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 ROTATE_BYTES = 1 << 30        # weight replicas rotate until they span 1 GiB
 
 
@@ -79,6 +80,9 @@ def parse():
     ap.add_argument("--paired", action="store_true",
                     help="paired 4:8 weights (2.75 bits per weight) on the sparse MFMA instead of "
                          "the unconstrained 4:8 format")
+    ap.add_argument("--w4a4", action="store_true",
+                    help="NVFP4 activations (W4A4): tokens quantized once per step, gathered as "
+                         "FP4 rows into the first GEMM; the SwiGLU output quantized for the down GEMM")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain gather copy of known size (moesq_unpermute without "
                          "weights over 512 MiB in, 512 MiB out) to scale HBM byte counters")
@@ -150,8 +154,8 @@ def pack_on_gpu(m, wl, proj, chunk=16, paired=False):
 class Step:
     """Buffers and launches of one pass of the hot path."""
 
-    def __init__(self, m, wl, fused=True, paired=False, separate_route=False):
-        self.m, self.wl, self.fused = m, wl, fused
+    def __init__(self, m, wl, fused=True, paired=False, separate_route=False, w4a4=False):
+        self.m, self.wl, self.fused, self.w4a4 = m, wl, fused, w4a4
         dev = torch.device("cuda")
         ids, tw = synth.routing(wl)
         self.ids_host = ids
@@ -183,13 +187,20 @@ class Step:
         else:
             self.y = torch.empty(M, wl.proj[0][1], **bf)
         self.out = torch.empty(T if wl.weighted_combine else M, self.y.shape[1], **bf)
-        # decode batches route inside the first GEMM's launch
-        self.route_in_gemm = fused and not separate_route and M <= 1024 and M <= 4 * E
+        # W4A4: the tokens' NVFP4 rows, and the SwiGLU output's for the down GEMM
+        if w4a4:
+            self.xq = m.Act4.empty(T, wl.K_in)
+            self.hq = m.Act4.empty(M, wl.proj[0][1] // 2) if wl.swiglu else None
+        # decode batches route inside the first GEMM's launch (bf16 activations)
+        self.route_in_gemm = (fused and not separate_route and not w4a4 and M <= 1024
+                              and M <= 4 * E)
         # without router weights the combine is a pure scatter to flat order:
         # with dispatch fused, the GEMM's epilogue stores there directly
         self.scatter_in_gemm = fused and not wl.weighted_combine and not wl.swiglu
         self.names = (([] if self.route_in_gemm else ["route"]) + ([] if fused else ["permute"])
-                      + [f"gemm_{p[0]}" for p in wl.proj]
+                      + (["quantize_x"] if w4a4 else []) + [f"gemm_{wl.proj[0][0]}"]
+                      + (["quantize_h"] if w4a4 and wl.swiglu else [])
+                      + [f"gemm_{p[0]}" for p in wl.proj[1:]]
                       + ([] if self.scatter_in_gemm else ["combine"]))
 
     def calls(self):
@@ -205,9 +216,16 @@ class Step:
         if not self.fused:
             calls.append(lambda: m.moesq_permute(self.x, self.perm, wl.T, wl.k, wl.K_in, self.xr))
 
+        if self.w4a4:
+            calls.append(lambda: m.moesq_quantize_activations(self.x, wl.T, wl.K_in, self.xq.codes,
+                                                              self.xq.scales, self.xq.row_scale))
+
         def first(epi, out):
             # routing and dispatch fused into the first GEMM, dispatch fused,
             # or the routed copy
+            if self.w4a4:
+                return lambda: m.moesq_grouped_spgemm_act4(self.xq, self.perm, wl.T, wl.k, self.off,
+                                                           wl.M, w[0], epi, out)
             if self.route_in_gemm:
                 return lambda: m.moesq_route_grouped_spgemm(self.ids, self.x, wl.T, wl.k, w[0], epi,
                                                             out, self.off, self.perm, self.inv)
@@ -218,8 +236,15 @@ class Step:
 
         if wl.swiglu:
             calls.append(first(m.EPI_SWIGLU, self.h))
-            calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, w[1],
-                                                        m.EPI_NONE, self.y))
+            if self.w4a4:
+                calls.append(lambda: m.moesq_quantize_activations(self.h, wl.M, self.h.shape[1],
+                                                                  self.hq.codes, self.hq.scales,
+                                                                  self.hq.row_scale))
+                calls.append(lambda: m.moesq_grouped_spgemm_act4(self.hq, None, 0, 1, self.off, wl.M,
+                                                                 w[1], m.EPI_NONE, self.y))
+            else:
+                calls.append(lambda: m.moesq_grouped_spgemm(self.h, self.off, wl.M, w[1],
+                                                            m.EPI_NONE, self.y))
         elif self.scatter_in_gemm:
             calls.append(first(m.EPI_NONE | m.OUT_FLAT, self.out))
         else:
@@ -336,7 +361,11 @@ def gemm_source_sha():
     return hashlib.sha256(src).hexdigest()
 
 
-def measured_counters(workload, proj_name, paired=False):
+def counter_key(workload, proj_name, paired=False, w4a4=False):
+    return f"{workload}/{proj_name}" + ("/paired" if paired else "") + ("/w4a4" if w4a4 else "")
+
+
+def measured_counters(workload, proj_name, paired=False, w4a4=False):
     """Per-call counter figures of the grouped GEMM from the committed
     rocprofv3 summary (traffic_bytes, mfma_flops, ...), or {} when the GEMM
     source has changed since the counters were taken (or no summary covers
@@ -348,7 +377,7 @@ def measured_counters(workload, proj_name, paired=False):
         return {}
     if gemm_source_sha() != rec.get("source_sha256"):
         return {}
-    return rec.get("kernels", {}).get(f"{workload}/{proj_name}" + ("/paired" if paired else ""), {})
+    return rec.get("kernels", {}).get(counter_key(workload, proj_name, paired, w4a4), {})
 
 
 def _kernel_tile(name):
@@ -364,7 +393,8 @@ def record_counters(root):
     """Turns rocprofv3 counter CSVs into profiles/spgemm_counters.json.
 
     Layout: root/<case>/<pass>/.../*counter_collection.csv with case a
-    workload name, <workload>_paired, or calibrate (bench.py
+    workload name with the suffixes _paired and _w4a4 of the bench options
+    it ran with, or calibrate (bench.py
     --calibrate-copy).  Per kernel: the mean over its dispatches of each
     counter; per GEMM call: the sum over the kernels of that projection (one
     to three launches).  HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB) times
@@ -410,8 +440,11 @@ def record_counters(root):
     for case, kernels in sorted(per.items()):
         if case == "calibrate":
             continue
-        paired = case.endswith("_paired")
-        wl = synth.WORKLOADS[case[:-len("_paired")] if paired else case]
+        name = case
+        w4a4 = name.endswith("_w4a4")
+        name = name[:-len("_w4a4")] if w4a4 else name
+        paired = name.endswith("_paired")
+        wl = synth.WORKLOADS[name[:-len("_paired")] if paired else name]
         for p, (pname, _, _) in enumerate(wl.proj):
             acc = defaultdict(float)
             names = []
@@ -431,7 +464,7 @@ def record_counters(root):
             rec.update({c: round(v, 2) for c, v in acc.items()})
             if "FETCH_SIZE" in acc and "WRITE_SIZE" in acc:
                 rec["traffic_bytes"] = acc["FETCH_SIZE"] * 1024 * ff + acc["WRITE_SIZE"] * 1024 * wf
-            out["kernels"][f"{wl.name}/{pname}" + ("/paired" if paired else "")] = rec
+            out["kernels"][counter_key(wl.name, pname, paired, w4a4)] = rec
     with open(COUNTERS_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(f"wrote {COUNTERS_JSON}: {sorted(out['kernels'])}")
@@ -460,7 +493,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(wl, budget_s, paired=False):
+def cpu_baseline(wl, budget_s, paired=False, w4a4=False):
     """The CPU oracle on the same workload, each phase timed on its own.
 
     Route, permute and the combine run on the whole workload (data movement;
@@ -479,7 +512,8 @@ def cpu_baseline(wl, budget_s, paired=False):
         threads = os.cpu_count()
     ids, tw = synth.routing(wl)
     x = synth.tokens(wl).to(torch.float64).numpy()
-    ph = dict.fromkeys(["route", "permute", "compress", "decode", "gemm", "swiglu", "combine"], 0.0)
+    ph = dict.fromkeys(["route", "permute", "compress", "decode", "quantize", "gemm", "swiglu",
+                        "combine"], 0.0)
 
     t = time.perf_counter()
     off, perm, inv = oracle.route(ids, wl.E)
@@ -516,6 +550,10 @@ def cpu_baseline(wl, budget_s, paired=False):
             t = time.perf_counter()
             Wd = oracle.decode_paired(pk) if paired else oracle.decode(pk)
             ph["decode"] += time.perf_counter() - t
+            if w4a4:
+                t = time.perf_counter()
+                a = oracle.decode_activations(oracle.quantize_activations(a))
+                ph["quantize"] += time.perf_counter() - t
             t = time.perf_counter()
             y = oracle.expert_gemm(a, Wd)
             ph["gemm"] += time.perf_counter() - t
@@ -529,8 +567,10 @@ def cpu_baseline(wl, budget_s, paired=False):
         experts += 1
     prefill = wl.M >= 4096
     scale = flops_all / flops if prefill else bytes_all / wbytes
-    total = ph["route"] + ph["permute"] + ph["combine"] + scale * (ph["decode"] + ph["gemm"] + ph["swiglu"])
-    sample = (f"route, permute and combine of all {wl.M} routed rows; decode + float64 GEMM"
+    total = ph["route"] + ph["permute"] + ph["combine"] + scale * (ph["decode"] + ph["quantize"]
+                                                                  + ph["gemm"] + ph["swiglu"])
+    sample = (f"route, permute and combine of all {wl.M} routed rows; decode"
+              f"{' + NVFP4 activation quantization' if w4a4 else ''} + float64 GEMM"
               f"{' + SwiGLU' if wl.swiglu else ''} of the {experts} experts with the most rows "
               f"({rows_done} rows), scaled x{scale:.1f} to all {active} active experts")
     phases = {k: round(v, 4) for k, v in ph.items()}
@@ -558,8 +598,10 @@ def main():
         sweep(m, wl, Gs=tuple(int(v) for v in args.sweep_experts.split(",")),
               Rs=tuple(int(v) for v in args.sweep_rows.split(",")), paired=args.paired)
         return
+    if args.w4a4 and args.unfused:
+        sys.exit("--w4a4 gathers the quantized tokens inside the GEMM; --unfused does not apply")
     step = Step(m, wl, fused=not args.unfused, paired=args.paired,
-                separate_route=args.separate_route)
+                separate_route=args.separate_route, w4a4=args.w4a4)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step.run()
@@ -599,7 +641,7 @@ def main():
     g0 = f"gemm_{wl.proj[0][0]}"
     g0_ms = kernel_ms[g0]
     f0, b0 = work[0]
-    cnt = measured_counters(wl.name, wl.proj[0][0], args.paired)
+    cnt = measured_counters(wl.name, wl.proj[0][0], args.paired, args.w4a4)
     if prefill:
         # The method's own work: one multiply-add per kept weight (half of the
         # N x K weights) per routed row, i.e. M*N*K flops per projection.
@@ -615,6 +657,13 @@ def main():
         roof["mfma_executed_tflops"] = None if mf is None else mf / (g0_ms * 1e-3) / 1e12
         roof["mfma_executed_frac"] = (None if mf is None
                                       else roof["mfma_executed_tflops"] / PEAK_BF16_TFLOPS)
+        if args.w4a4:
+            # NVFP4 operands with E4M3 block scales run on the bf16 MFMA after
+            # an exact decode (the FP4 MFMA takes power-of-two block scales
+            # only); the FP4 peak is shown for reference.
+            roof["mfma_dtype"] = "bf16 (NVFP4 activations decoded exactly)"
+            roof["fp4_peak"] = PEAK_FP4_TFLOPS
+            roof["frac_of_fp4_peak"] = roof["achieved"] / PEAK_FP4_TFLOPS
     else:
         roof = {"bound": "hbm", "achieved": b0 / (g0_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -634,14 +683,17 @@ def main():
            "config": {"workload": wl.name, "E": wl.E, "T": wl.T, "k": wl.k, "routed_rows": wl.M,
                       "projections": [list(p) for p in wl.proj], "routing": wl.bias,
                       "active_experts": active, "parallelism": "none",
-                      "weights": "paired 4:8 (2.75 bpw)" if args.paired else "4:8 (3.25 bpw)"},
+                      "weights": "paired 4:8 (2.75 bpw)" if args.paired else "4:8 (3.25 bpw)",
+                      "activations": ("NVFP4 (E2M1, E4M3 per 32 positions, fp32 per row)"
+                                      if args.w4a4 else "bf16")},
            "kernel_ms": kernel_ms,
            "weight_replicas": len(step.replicas),
            "gemm_tflops_dense_equiv": total_flops / 1e12,
            "weight_gb_active": total_wbytes / 1e9,
            "roofline": roof}
     if not args.no_cpu_baseline:
-        work, dt, threads, sample, phases = cpu_baseline(wl, args.cpu_seconds, args.paired)
+        work, dt, threads, sample, phases = cpu_baseline(wl, args.cpu_seconds, args.paired,
+                                                         args.w4a4)
         cv = work / dt / 1e12 if prefill else work / dt / 1e9
         res["cpu_baseline"] = {"value": cv, "unit": unit, "cores": threads, "kind": "oracle",
                                "sample": sample, "seconds_full_step": dt, "phases_s": phases,

@@ -289,6 +289,67 @@ moesq_status_t moesq_route_grouped_spgemm(const int32_t *topk_ids, const uint16_
                                           int32_t *inv_perm, hipStream_t stream);
 
 /*
+ * NVFP4 activations for the W4A4 expert GEMM ("D.1 Implementation details":
+ * the serving integration quantizes the activations of the expert GEMM in
+ * 32-element scale blocks; "3.4 Implementation details": weights and
+ * quantized activations are packed in corresponding scale blocks; "B
+ * Experimental setup", Compression scope: paired 4:8 NVFP4 W4A4 with
+ * 32-element blocks).  Rows of K activations (K % 32 == 0):
+ *
+ *   codes     [rows][K/2]  E2M1 codes, two per byte, position 2i in the low nibble
+ *   scales    [rows][K/32] E4M3 scale (sign 0) of positions [32b, 32b+32),
+ *                          the same K blocks as the weights' scales
+ *   row_scale [rows]       fp32 second-level scale of the row
+ *
+ *   x~[r][k] = E2M1(code) * E4M3(scale of k's block) * row_scale[r]
+ *
+ * The struct is a host object; its pointers are device pointers.
+ */
+typedef struct {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const float *row_scale;
+  int32_t rows, K;
+} moesq_act4_t;
+
+/*
+ * Quantize bf16 activation rows to NVFP4 (the layout above), one row on its
+ * own, every decision in fp32 with ties to the even code:
+ *   row_scale[t] = amax_t / 2688 (2688 = 6*448; 1 for a zero row)
+ *   scales[t][b] = E4M3(amax_b / (6 * row_scale[t])), saturating at 448
+ *   code         = E2M1(x / (E4M3(scale) * row_scale[t])), saturating at 6;
+ *                  0 where that product is 0; zero is +0
+ *   x [T][K] bf16 in; codes [T][K/2], scales [T][K/32], row_scale [T] out.
+ * Inputs must be finite.  x and codes 16-byte aligned (MOESQ_ERR_ARG).
+ * Limits: K % 32 == 0, K > 0, T >= 0.
+ */
+moesq_status_t moesq_quantize_activations(const uint16_t *x, int32_t T, int32_t K,
+                                          uint8_t *codes, uint8_t *scales, float *row_scale,
+                                          hipStream_t stream);
+
+/*
+ * W4A4 grouped GEMM: moesq_grouped_spgemm (perm == NULL) or
+ * moesq_grouped_spgemm_gather (perm != NULL) with NVFP4 activations instead
+ * of bf16 ones:
+ *   acc[r][n] = sum_k x~[src(r)][k] * W~_e[n][k]   (fp32 accumulation; the
+ *               decoded bf16 operands E2M1*E4M3 are exact)
+ *   y as moesq_grouped_spgemm with g = global_scale[e] * row_scale[src(r)]
+ *   src(r) = perm[r] / k with a gather permutation (x->rows == T, M == T*k;
+ *   the quantized tokens are gathered inside the GEMM, as moesq_permute would
+ *   copy their bf16 rows), else r (x->rows == M: rows in routed order, such
+ *   as the quantized SwiGLU output feeding the down projection).
+ *   MOESQ_OUT_FLAT as for the gather call (needs perm).
+ *   x: host descriptor, x->K == w->K.  Other arguments and limits as
+ *   moesq_grouped_spgemm_gather / moesq_grouped_spgemm; rows of y outside
+ *   every expert range are not written; perm entries outside [0, T*k) give
+ *   zero rows.
+ */
+moesq_status_t moesq_grouped_spgemm_act4(const moesq_act4_t *x, const int32_t *perm, int32_t T,
+                                         int32_t k, const int32_t *expert_offsets, int32_t M,
+                                         const moesq_weights_t *w, int32_t epilogue, uint16_t *y,
+                                         hipStream_t stream);
+
+/*
  * Combine.
  *   topk_weights != NULL: out[t][:] = bf16_rne( sum_{j<k} w[t*k+j] * y[inv_perm[t*k+j]][:] ),
  *                         fp32 accumulation in j order; out is [T][N].

@@ -55,6 +55,11 @@ struct SpgemmArgs {
   const int32_t *ids;
   int32_t *route_offsets, *route_perm, *route_inv;
   int flat;   // store result row r at y[perm[r]] (flat order) instead of y[r]
+  // NVFP4 activations (W4A4): codes [rows][K/2], E4M3 scales [rows][K/32] and
+  // the fp32 row scales of the token rows (rows = T with a gather, else M)
+  const uint8_t *aq_codes;
+  const uint8_t *aq_scales;
+  const float *aq_g;
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -369,7 +374,8 @@ __host__ __device__ inline size_t spgemm_sched_bytes(int E) {
   return ((size_t)(2 * E + 1) * 4 + (size_t)E * 2 + 15) & ~(size_t)15;
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false,
+          bool ACT4 = false>
 __global__ __launch_bounds__(WAVES * 64)
 // 16-row tiles stream weights: at most 128 VGPRs, so that four 4-wave
 // workgroups share a CU.  32-row tiles hold 128 accumulators per lane.
@@ -713,14 +719,103 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     uint32_t srow[BPW];
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
-      const int r = tok0 + min((wave * BPW + j) * (64 / UPR) + lane / UPR, ntok - 1);
-      int src = r;
+      srow[j] = 0;
+      if constexpr (!ACT4) {
+        const int r = tok0 + min((wave * BPW + j) * (64 / UPR) + lane / UPR, ntok - 1);
+        int src = r;
+        if (ROUTE || a.perm) {
+          const int pi = perm_at(r);
+          src = (pi >= 0 && pi < a.T * a.k) ? pi / a.k : 0;
+        }
+        srow[j] = (uint32_t)src * (uint32_t)K;
+      }
+    }
+    // NVFP4 activations (W4A4): each chunk, thread tid stages one 32-position
+    // block (16 code bytes and its E4M3 scale) of token-tile row a_tr: the
+    // loads go to registers while the previous chunk computes, then the
+    // block is decoded exactly to bf16 (E2M1 * E4M3 has at most six
+    // significant bits) and written into the tile layout the MFMA loop
+    // reads; the row's fp32 scale is applied in the epilogue.  Rows past the
+    // routed ones repeat the last routed row, blocks past K are zero.
+    constexpr int BPR = KC / 32;                      // blocks per row of a chunk
+    static_assert(!ACT4 || BM * BPR <= WAVES * 64, "one activation block per thread and chunk");
+    const int a_tr = tid / BPR, a_jb = tid - (tid / BPR) * BPR;
+    const bool a_on = ACT4 && tid < BM * BPR && a_tr < nrows;
+    const uint32_t nbk = (uint32_t)(K >> 5);
+    uint32_t a_vo = 0, a_so = 0;
+    if constexpr (ACT4) {
+      int src = tok0 + min(a_tr, ntok - 1);
       if (ROUTE || a.perm) {
-        const int pi = perm_at(r);
+        const int pi = perm_at(src);
         src = (pi >= 0 && pi < a.T * a.k) ? pi / a.k : 0;
       }
-      srow[j] = (uint32_t)src * (uint32_t)K;
+      a_vo = (uint32_t)src * (uint32_t)(K >> 1) + (uint32_t)a_jb * 16u;
+      a_so = (uint32_t)src * nbk + (uint32_t)a_jb;
     }
+    const uint32_t arows = ACT4 ? (uint32_t)((ROUTE || a.perm) ? a.T : a.M) : 0u;
+    const __amdgpu_buffer_rsrc_t acr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.aq_codes, 0, (int)(arows * (uint32_t)(K >> 1)), 0x20000);
+    const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)a.aq_scales, 0, (int)(arows * nbk), 0x20000);
+    struct AReg {
+      u32x4_t c;
+      uint32_t s;
+    };
+    auto act_load = [&](AReg &r, int k0) {
+      const uint32_t kb = (uint32_t)(k0 >> 5) + (uint32_t)a_jb;
+      if (a_on && kb < nbk) {
+        r.c = __builtin_amdgcn_raw_buffer_load_b128(acr, a_vo, (uint32_t)k0 >> 1, 0);
+        r.s = __builtin_amdgcn_raw_buffer_load_b8(asr, a_so, (uint32_t)k0 >> 5, 0);
+      } else {
+        r.c = u32x4_t{0u, 0u, 0u, 0u};
+        r.s = 0u;
+      }
+    };
+    // Decode and LDS writes (asm: the writes must not wait for direct-to-LDS
+    // weight loads still in flight; the caller waits for them before its
+    // barrier).  4:8 weights: unit c of a row at slot c ^ (row % UPR), dword d
+    // of a unit = positions 2d, 2d+1.  Paired weights: a 16-position unit u
+    // (groups G, G') as its even half [G 0 2 4 6 | G' 0 2 4 6] at slot
+    // (2u) ^ (row % UPR) and its odd half at slot (2u + 1) ^ (row % UPR).
+    auto act_store = [&](uint16_t *buf, const AReg &r) {
+      if (!a_on) return;
+      const float sc = __builtin_amdgcn_cvt_f32_fp8(r.s, 0);
+      const uint32_t rowb = lds_addr(buf + a_tr * KC);
+      const uint32_t sw = (uint32_t)(a_tr & (UPR - 1));
+      auto up = [&](float v) { return __float_as_uint(v * sc); };
+      auto pk = [&](float lo, float hi) { return __builtin_amdgcn_perm(up(hi), up(lo), 0x07060302u); };
+      auto wr = [&](uint32_t slot, uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+        const u32x4_t v = {d0, d1, d2, d3};
+        asm volatile("ds_write_b128 %0, %1" ::"v"(rowb + 16u * (slot ^ sw)), "v"(v) : "memory");
+      };
+      if constexpr (!PAIRED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[i], 1.0f, 0);
+          const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[i], 1.0f, 1);
+          const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[i], 1.0f, 2);
+          const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.c[i], 1.0f, 3);
+          wr(4u * (uint32_t)a_jb + (uint32_t)i, pk(p0[0], p0[1]), pk(p1[0], p1[1]),
+             pk(p2[0], p2[1]), pk(p3[0], p3[1]));
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t G = r.c[2 * m], H = r.c[2 * m + 1];
+          const f32x2_t g0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(G, 1.0f, 0);
+          const f32x2_t g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(G, 1.0f, 1);
+          const f32x2_t g2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(G, 1.0f, 2);
+          const f32x2_t g3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(G, 1.0f, 3);
+          const f32x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(H, 1.0f, 0);
+          const f32x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(H, 1.0f, 1);
+          const f32x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(H, 1.0f, 2);
+          const f32x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(H, 1.0f, 3);
+          const uint32_t u = 2u * (uint32_t)a_jb + (uint32_t)m;
+          wr(2u * u, pk(g0[0], g1[0]), pk(g2[0], g3[0]), pk(h0[0], h1[0]), pk(h2[0], h3[0]));
+          wr(2u * u + 1u, pk(g0[1], g1[1]), pk(g2[1], g3[1]), pk(h0[1], h1[1]), pk(h2[1], h3[1]));
+        }
+      }
+    };
     // 4:8 weights: the token loads are buffer loads to LDS.  The byte offset
     // of the lane's row and 16-byte unit is fixed for the item (VGPR), the
     // chunk's K offset is uniform (SGPR), so a whole chunk costs no vector
@@ -909,9 +1004,16 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
             w.s[f] = sc;
           }
         };
-        load_tok(tkA, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if constexpr (PAIRED) split_tok(tkA);
+        AReg ar;
+        if constexpr (ACT4) {
+          act_load(ar, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          act_store(tkA, ar);
+        } else {
+          load_tok(tkA, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (PAIRED) split_tok(tkA);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         // One chunk: tokens of c + 1 and weights of c + 2 are issued in that
@@ -920,7 +1022,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         // weights of c + 2 in flight.  A bare barrier: every LDS write this
         // chunk makes (split, ring) is covered by the explicit waits.
         auto chunk = [&](int c, int slot, const uint16_t *cur, uint16_t *nxt) {
-          if (c + 1 < nk) load_tok(nxt, (c + 1) * KC);
+          if (c + 1 < nk) {
+            if constexpr (ACT4) act_load(ar, (c + 1) * KC);
+            else load_tok(nxt, (c + 1) * KC);
+          }
           if (c + 2 < nk) ring_load(slot == 0 ? 2 : slot - 1, (c + 2) * KC);
           WC wc;
           ring_read(wc, slot);
@@ -947,8 +1052,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING_LOADS) : "memory");
           else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          if constexpr (PAIRED)
-            if (c + 1 < nk) split_tok(nxt);
+          if (c + 1 < nk) {
+            if constexpr (ACT4) act_store(nxt, ar);
+            else if constexpr (PAIRED) split_tok(nxt);
+          }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
         };
@@ -965,16 +1072,24 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         }
       } else if constexpr (PAIRED) {
         PChunk<RF> wA = w0, wB;
-        load_tok(tkA, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        split_tok(tkA);
+        AReg ar;
+        if constexpr (ACT4) {
+          act_load(ar, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          act_store(tkA, ar);
+        } else {
+          load_tok(tkA, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          split_tok(tkA);
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the split's writes
         __syncthreads();
         auto chunk = [&](int c, const uint16_t *cur, uint16_t *nxt, PChunk<RF> &wc,
                          PChunk<RF> &wn) {
           if (c + 1 < nk) {
             load_pchunk(wn, vr, mr, sr, fv, fm, fs, tlo((c + 1) * KC));
-            load_tok(nxt, (c + 1) * KC);
+            if constexpr (ACT4) act_load(ar, (c + 1) * KC);
+            else load_tok(nxt, (c + 1) * KC);
           }
           if ((c + 1) * KC > K) {
             // segments past K were clamped to the last one: zero their codes
@@ -986,7 +1101,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           }
           mma_chunk_paired<MS, RF, NF, KC, FULL>(acc, cur, wc, nft, q, rl);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          if (c + 1 < nk) split_tok(nxt);
+          if (c + 1 < nk) {
+            if constexpr (ACT4) act_store(nxt, ar);
+            else split_tok(nxt);
+          }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the split's writes
           __syncthreads();
         };
@@ -996,8 +1114,16 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
         }
       } else {
         WChunk<RF, KQ> wA = w0, wB;
-        load_tok(tkA, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        AReg ar;
+        if constexpr (ACT4) {
+          act_load(ar, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          act_store(tkA, ar);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        } else {
+          load_tok(tkA, 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         __syncthreads();
         // One chunk: prefetch chunk c + 1 into (nxt, wn), compute chunk c from
         // (cur, wc).  The two token buffers are distinct LDS objects, so the
@@ -1006,7 +1132,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
                          WChunk<RF, KQ> &wn) {
           if (c + 1 < nk) {
             load_w(wn, (c + 1) * KC);
-            load_tok(nxt, (c + 1) * KC);
+            if constexpr (ACT4) act_load(ar, (c + 1) * KC);
+            else load_tok(nxt, (c + 1) * KC);
           }
           if constexpr (TILED) {
             if ((c + 1) * KC > K) {
@@ -1020,6 +1147,10 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
           }
           mma_chunk<MS, RF, NF, KC, FULL>(acc, cur, wc, lut, nft, q, rl);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (ACT4) {
+            if (c + 1 < nk) act_store(nxt, ar);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          }
           __syncthreads();
         };
         for (int c = 0; c < nk; c += 2) {
@@ -1032,21 +1163,25 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       // Epilogue.  Accumulator element r of a lane holds weight row
       // (r/4)*4*LG + 4q + r%4 of its fragment for token rl of its token
       // fragment: four consecutive rows per group of four, one 8-byte store.
-      const float g = a.gscale[e];
+      const float ge = a.gscale[e];
   #pragma unroll
       for (int t = 0; t < NF; ++t) {
         const int trow = t * MS + rl;
         if (trow >= ntok) continue;
         size_t out_r = (size_t)(tok0 + trow);
         bool keep = true;
+        int src = (int)out_r;   // the token row of the activations
         if (ROUTE || a.perm) {
           const int pi = perm_at((int)out_r);
           keep = pi >= 0 && pi < a.T * a.k;
+          src = keep ? pi / a.k : 0;
           if (a.flat) {   // scatter to the flat position; no destination: no store
             if (!keep) continue;
             out_r = (size_t)pi;
           }
         }
+        // W4A4: the activation row's fp32 scale joins the expert's
+        const float g = ACT4 ? ge * a.aq_g[src] : ge;
   #pragma unroll
         for (int r4 = 0; r4 < MF::NC / 4; ++r4) {
           const int roff = r4 * 4 * LG + 4 * q;
@@ -1099,10 +1234,11 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   }
 }
 
-template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false>
+template <int WAVES, int MS, int RF, int TF, int KC, bool SWIGLU, int FMT, bool ROUTE = false,
+          bool ACT4 = false>
 static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
-  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT, ROUTE>;
+  auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT, ROUTE, ACT4>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   // schedule arrays, then with fused routing its offsets, cursors and permutation
   const size_t dyn = spgemm_sched_bytes(a.E) + (ROUTE ? (size_t)(2 * a.E + 1 + a.M) * 4 : 0);
@@ -1155,47 +1291,54 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
 // Paired weights take the same tiles on the sparse MFMA (16x16x64 and
 // 32x32x32): the same token and weight-row counts per wave, each step
 // contracting twice the dense K.
-template <int FMT>
+template <int FMT, bool ACT4 = false>
 static moesq_status_t launch_layout(SpgemmArgs a, bool swiglu, hipStream_t stream) {
   const int out_rows = swiglu ? a.N / 2 : a.N;
   a.rows_lo = 0;
   a.rows_hi = INT_MAX;
   // decode batches: one launch of the one-fragment streaming tile
   if ((long long)a.M <= 4ll * a.E)
-    return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
-                  : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
+    return swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT, false, ACT4>(a, stream)
+                  : launch_one<4, 16, 2, 1, 256, false, FMT, false, ACT4>(a, stream);
   if (out_rows % 32 != 0)   // the 32-row tile needs whole 32-row fragments
-    return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
-                  : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+    return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT, false, ACT4>(a, stream)
+                  : launch_one<8, 16, 2, 2, 256, false, FMT, false, ACT4>(a, stream);
   // A GEMM under ~5e11 multiply-adds is too short to pay for a second
   // launch: one launch, its tile from the average rows per expert.
   if ((double)a.M * a.N * a.K < 5.5e11) {
     if ((long long)a.M <= 32ll * a.E)
-      return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
-                    : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
-    return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
-                  : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
+      return swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT, false, ACT4>(a, stream)
+                    : launch_one<8, 16, 2, 2, 256, false, FMT, false, ACT4>(a, stream);
+    return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT, false, ACT4>(a, stream)
+                  : launch_one<8, 32, 2, 4, 128, false, FMT, false, ACT4>(a, stream);
   }
   // otherwise launches split by each expert's own row count (read on the
   // device): up to 16 rows the one-fragment streaming tile, up to 32 the
   // two-fragment one, above that the contraction tile
   a.rows_hi = 16;
-  moesq_status_t st = swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT>(a, stream)
-                             : launch_one<4, 16, 2, 1, 256, false, FMT>(a, stream);
+  moesq_status_t st = swiglu ? launch_one<4, 16, 2, 1, 256, true, FMT, false, ACT4>(a, stream)
+                             : launch_one<4, 16, 2, 1, 256, false, FMT, false, ACT4>(a, stream);
   if (st != MOESQ_OK) return st;
   a.rows_lo = 16;
   a.rows_hi = 32;
-  st = swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT>(a, stream)
-              : launch_one<8, 16, 2, 2, 256, false, FMT>(a, stream);
+  st = swiglu ? launch_one<8, 16, 2, 2, 256, true, FMT, false, ACT4>(a, stream)
+              : launch_one<8, 16, 2, 2, 256, false, FMT, false, ACT4>(a, stream);
   if (st != MOESQ_OK) return st;
   a.rows_lo = 32;
   a.rows_hi = INT_MAX;
-  return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT>(a, stream)
-                : launch_one<8, 32, 2, 4, 128, false, FMT>(a, stream);
+  return swiglu ? launch_one<8, 32, 2, 4, 128, true, FMT, false, ACT4>(a, stream)
+                : launch_one<8, 32, 2, 4, 128, false, FMT, false, ACT4>(a, stream);
 }
 
 static moesq_status_t launch_spgemm(const SpgemmArgs &a, bool swiglu, int layout,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, bool act4 = false) {
+  if (act4) {
+    switch (layout) {
+      case MOESQ_LAYOUT_TILED: return launch_layout<FMT_TILED, true>(a, swiglu, stream);
+      case MOESQ_LAYOUT_PAIRED_TILED: return launch_layout<FMT_PAIRED, true>(a, swiglu, stream);
+      default: return launch_layout<FMT_CANONICAL, true>(a, swiglu, stream);
+    }
+  }
   switch (layout) {
     case MOESQ_LAYOUT_TILED: return launch_layout<FMT_TILED>(a, swiglu, stream);
     case MOESQ_LAYOUT_PAIRED_TILED: return launch_layout<FMT_PAIRED>(a, swiglu, stream);
@@ -1236,7 +1379,7 @@ extern "C" size_t moesq_spgemm_workspace_bytes(int32_t, const moesq_weights_t *)
 static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int32_t *perm, int32_t T,
                                    int32_t k, const int32_t *expert_offsets, int32_t M,
                                    const moesq_weights_t *w, int32_t epilogue, uint16_t *y,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const moesq_act4_t *xq = nullptr) {
   clear_error();
   moesq_status_t st = check_weights(w, who);
   if (st != MOESQ_OK) return st;
@@ -1251,10 +1394,19 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   if (M < 0) return fail(MOESQ_ERR_SHAPE, std::string(who) + ": M must be >= 0");
   if (!expert_offsets) return fail(MOESQ_ERR_NULL, std::string(who) + ": expert_offsets is NULL");
   if (M == 0) return MOESQ_OK;
-  if (!x || !y) return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL input or output rows");
+  if ((!x && !xq) || !y) return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL input or output rows");
   // token rows are addressed by 32-bit element offsets
   if ((long long)(perm ? T : M) * w->K > 0x7fffffffll)
     return fail(MOESQ_ERR_SHAPE, std::string(who) + ": rows of x times K must stay under 2^31");
+  if (xq) {
+    if (!xq->codes || !xq->scales || !xq->row_scale)
+      return fail(MOESQ_ERR_NULL, std::string(who) + ": NULL activation codes, scales or row scales");
+    if (xq->K != w->K)
+      return fail(MOESQ_ERR_SHAPE, std::string(who) + ": activation K differs from the weights' K");
+    if (xq->rows != (perm ? T : M))
+      return fail(MOESQ_ERR_SHAPE, std::string(who) + ": activation rows must be T with a gather "
+                                                      "permutation, else M");
+  }
   SpgemmArgs a{};
   a.x = x;
   a.perm = perm;
@@ -1271,7 +1423,12 @@ static moesq_status_t spgemm_entry(const char *who, const uint16_t *x, const int
   a.N = w->N;
   a.K = w->K;
   a.flat = flat;
-  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout, stream);
+  if (xq) {
+    a.aq_codes = xq->codes;
+    a.aq_scales = xq->scales;
+    a.aq_g = xq->row_scale;
+  }
+  return launch_spgemm(a, epilogue == MOESQ_EPI_SWIGLU, w->layout, stream, xq != nullptr);
 }
 
 extern "C" moesq_status_t moesq_grouped_spgemm(const uint16_t *x_routed,
@@ -1367,4 +1524,21 @@ extern "C" moesq_status_t moesq_grouped_spgemm_gather(const uint16_t *x, const i
   if (T > 0 && !perm) return fail(MOESQ_ERR_NULL, "moesq_grouped_spgemm_gather: perm is NULL");
   return spgemm_entry("moesq_grouped_spgemm_gather", x, perm, T, k, expert_offsets, T * k, w,
                       epilogue, y, stream);
+}
+
+extern "C" moesq_status_t moesq_grouped_spgemm_act4(const moesq_act4_t *x, const int32_t *perm,
+                                                    int32_t T, int32_t k,
+                                                    const int32_t *expert_offsets, int32_t M,
+                                                    const moesq_weights_t *w, int32_t epilogue,
+                                                    uint16_t *y, hipStream_t stream) {
+  static const char *who = "moesq_grouped_spgemm_act4";
+  clear_error();
+  if (!x) return fail(MOESQ_ERR_NULL, std::string(who) + ": activation descriptor is NULL");
+  if (perm) {
+    if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffll)
+      return fail(MOESQ_ERR_SHAPE, std::string(who) + ": need T >= 0, k >= 1, T*k < 2^31");
+    if ((long long)T * k != M)
+      return fail(MOESQ_ERR_SHAPE, std::string(who) + ": with a gather permutation M must be T*k");
+  }
+  return spgemm_entry(who, nullptr, perm, T, k, expert_offsets, M, w, epilogue, y, stream, x);
 }

@@ -40,6 +40,11 @@ class WeightsDesc(ctypes.Structure):
                 ("E", _i32), ("N", _i32), ("K", _i32), ("layout", _i32)]
 
 
+class Act4Desc(ctypes.Structure):
+    """moesq_act4_t."""
+    _fields_ = [("codes", _vp), ("scales", _vp), ("row_scale", _vp), ("rows", _i32), ("K", _i32)]
+
+
 def _sig(name, restype, *argtypes):
     f = getattr(_lib, name)
     f.restype = restype
@@ -58,6 +63,9 @@ _spgemm_gather = _sig("moesq_grouped_spgemm_gather", _i32, _vp, _vp, _i32, _i32,
                       ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _sz, _vp)
 _route_spgemm = _sig("moesq_route_grouped_spgemm", _i32, _vp, _vp, _i32, _i32,
                      ctypes.POINTER(WeightsDesc), _i32, _vp, _vp, _vp, _vp, _vp)
+_quant_act = _sig("moesq_quantize_activations", _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp)
+_spgemm_act4 = _sig("moesq_grouped_spgemm_act4", _i32, ctypes.POINTER(Act4Desc), _vp, _i32, _i32,
+                    _vp, _i32, ctypes.POINTER(WeightsDesc), _i32, _vp, _vp)
 _unpermute = _sig("moesq_unpermute", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _pack = _sig("moesq_pack_weights", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp)
 _pack_paired = _sig("moesq_pack_weights_paired", _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -75,6 +83,7 @@ EXPORTED = ["moesq_route", "moesq_route_workspace_bytes", "moesq_route_noalloc",
             "moesq_permute",
             "moesq_grouped_spgemm", "moesq_spgemm_workspace_bytes",
             "moesq_grouped_spgemm_gather", "moesq_route_grouped_spgemm", "moesq_unpermute",
+            "moesq_quantize_activations", "moesq_grouped_spgemm_act4",
             "moesq_pack_weights", "moesq_pack_weights_paired", "moesq_tile_weights",
             "moesq_decode_weights",
             "moesq_validate", "moesq_stream_read", "moesq_status_string",
@@ -184,6 +193,28 @@ class Weights:
                        torch.empty(E, dtype=torch.float32, device=device), layout)
 
 
+class Act4:
+    """Device tensors of NVFP4 activation rows (W4A4): codes uint8 [rows, K/2],
+    scales uint8 [rows, K/32], row_scale float32 [rows]."""
+
+    def __init__(self, codes, scales, row_scale):
+        rows, K2 = codes.shape
+        self.rows, self.K = int(rows), int(K2) * 2
+        for t, shape, name in [(scales, (rows, self.K // 32), "scales"), (row_scale, (rows,), "row_scale")]:
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        self.codes, self.scales, self.row_scale = codes, scales, row_scale
+        self.desc = Act4Desc(_ptr(codes, torch.uint8, "codes", True),
+                             _ptr(scales, torch.uint8, "scales", True),
+                             _ptr(row_scale, torch.float32, "row_scale", True), self.rows, self.K)
+
+    @staticmethod
+    def empty(rows: int, K: int, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        return Act4(torch.empty(rows, K // 2, **u8), torch.empty(rows, K // 32, **u8),
+                    torch.empty(rows, dtype=torch.float32, device=device))
+
+
 # ------------------------------------------------------------ C-ABI mirrors
 
 def moesq_route(topk_ids, T: int, k: int, E: int, expert_offsets, perm, inv_perm,
@@ -267,6 +298,28 @@ def moesq_unpermute(y, inv_perm, topk_weights, T: int, k: int, N: int, out, stre
     _check(_unpermute(_ptr(y, torch.bfloat16, "y"), _ptr(inv_perm, torch.int32, "inv_perm"),
                       _ptr(topk_weights, torch.float32, "topk_weights", True), T, k, N,
                       _ptr(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def moesq_quantize_activations(x, T: int, K: int, codes, scales, row_scale, stream=None):
+    _sizes((x, T * K, "x"), (codes, T * K // 2, "codes"), (scales, T * K // 32, "scales"),
+           (row_scale, T, "row_scale"))
+    _check(_quant_act(_ptr(x, torch.bfloat16, "x", True), T, K,
+                      _ptr(codes, torch.uint8, "codes", True), _ptr(scales, torch.uint8, "scales", True),
+                      _ptr(row_scale, torch.float32, "row_scale", True), _stream(stream)))
+
+
+def moesq_grouped_spgemm_act4(x: Act4, perm, T: int, k: int, expert_offsets, M: int, w: Weights,
+                              epilogue: int, y, stream=None):
+    _sizes((perm, M, "perm"), (expert_offsets, w.E + 1, "expert_offsets"),
+           (y, M * _out_cols(w, epilogue), "y"))
+    if x.K != w.K:
+        raise ValueError(f"activations have K = {x.K}, the weights {w.K}")
+    if x.rows != (T if perm is not None else M):
+        raise ValueError(f"activations have {x.rows} rows, need {T if perm is not None else M}")
+    _check(_spgemm_act4(ctypes.byref(x.desc), _ptr(perm, torch.int32, "perm", True), T, k,
+                        _ptr(expert_offsets, torch.int32, "expert_offsets"), M,
+                        ctypes.byref(w.desc), epilogue, _ptr(y, torch.bfloat16, "y", True),
+                        _stream(stream)))
 
 
 def moesq_pack_weights(dense, E: int, N: int, K: int, values, masks, scales, global_scale,
@@ -403,6 +456,32 @@ def route_grouped_spgemm(topk_ids, x, k: int, w: Weights, epilogue: int = EPI_NO
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     moesq_route_grouped_spgemm(topk_ids, x, T, k, w, epilogue, out, off, perm, inv, stream)
     return out, off, perm, inv
+
+
+def quantize_activations(x, stream=None) -> Act4:
+    """bf16 [T, K] on the GPU -> its NVFP4 rows (Act4)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, K], got {tuple(x.shape)}")
+    T, K = x.shape
+    q = Act4.empty(T, K, device=x.device)
+    moesq_quantize_activations(x, T, K, q.codes, q.scales, q.row_scale, stream)
+    return q
+
+
+def grouped_spgemm_act4(xq: Act4, expert_offsets, w: Weights, epilogue: int = EPI_NONE, perm=None,
+                        k: int = 1, out=None, stream=None):
+    """W4A4 grouped GEMM.  With `perm`, routed row r reads quantized token
+    perm[r] // k of xq (dispatch fused; rows = T*k); else xq's rows are the
+    routed rows."""
+    M = xq.rows * k if perm is not None else xq.rows
+    n_out = _out_cols(w, epilogue)
+    if out is None:
+        out = torch.empty(M, n_out, dtype=torch.bfloat16, device=xq.codes.device)
+    elif tuple(out.shape) != (M, n_out):
+        raise ValueError(f"out must be [{M}, {n_out}], got {tuple(out.shape)}")
+    moesq_grouped_spgemm_act4(xq, perm, xq.rows if perm is not None else 0, k, expert_offsets, M, w,
+                              epilogue, out, stream)
+    return out
 
 
 def unpermute(y, inv_perm, topk_weights, T: int, k: int, stream=None):

@@ -15,7 +15,7 @@ LIB = os.path.join(ROOT, "sparse_fp4_expert_amd", "libmoesq.so")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moesq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moesq_[a-z_0-9]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -252,3 +252,29 @@ def test_binding_rejects_mismatched_sizes(m):
             case()
         msg = str(ei.value)
         assert "on the GPU" not in msg, (i, msg)
+
+
+def test_w4a4_calls_reject(m):
+    ref = ctypes.byref
+    q = m._quant_act
+    assert q(0x10, 4, 48, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE        # K % 32
+    assert q(0x10, -1, 64, 0x10, 0x10, 0x10, None) == m.ERR_SHAPE       # T < 0
+    assert q(None, 4, 64, 0x10, 0x10, 0x10, None) == m.ERR_NULL
+    assert q(0x10, 4, 64, 0x10, 0x10, None, None) == m.ERR_NULL          # row scales
+    assert q(0x18, 4, 64, 0x10, 0x10, 0x10, None) == m.ERR_ARG           # misaligned x
+    assert q(None, 0, 64, None, None, None, None) == m.OK                # nothing to do
+    g = m._spgemm_act4
+    d = ref(_desc(m))                                                    # E=8, N=128, K=256
+    act = m.Act4Desc(0x10, 0x10, 0x10, 8, 256)
+    assert g(None, None, 0, 1, 0x10, 8, d, 0, 0x10, None) == m.ERR_NULL  # no activation descriptor
+    assert g(ref(m.Act4Desc(0x10, 0x10, 0x10, 8, 128)), None, 0, 1, 0x10, 8, d, 0, 0x10,
+             None) == m.ERR_SHAPE                                        # K differs
+    assert b"K differs" in m._last_error()
+    assert g(ref(m.Act4Desc(0x10, 0x10, 0x10, 7, 256)), None, 0, 1, 0x10, 8, d, 0, 0x10,
+             None) == m.ERR_SHAPE                                        # rows != M
+    assert g(ref(act), 0x10, 4, 2, 0x10, 9, d, 0, 0x10, None) == m.ERR_SHAPE   # M != T*k
+    assert g(ref(m.Act4Desc(None, 0x10, 0x10, 8, 256)), None, 0, 1, 0x10, 8, d, 0, 0x10,
+             None) == m.ERR_NULL                                         # codes NULL
+    assert g(ref(act), None, 0, 1, 0x10, 8, d, 5, 0x10, None) == m.ERR_ARG    # epilogue
+    assert g(ref(act), None, 0, 1, 0x10, 8, d, m.OUT_FLAT, 0x10, None) == m.ERR_ARG  # flat needs perm
+    assert g(ref(act), None, 0, 1, 0x10, 0, d, 0, None, None) == m.OK          # M = 0

@@ -88,10 +88,11 @@ def test_record_counters_sums_launches_and_scales(tmp_path, monkeypatch):
 import pytest  # noqa: E402
 
 
-@pytest.mark.parametrize("paired", [False, True])
-def test_cpu_baseline_tiny(paired):
+@pytest.mark.parametrize("paired,w4a4", [(False, False), (True, False), (False, True)])
+def test_cpu_baseline_tiny(paired, w4a4):
     wl = synth.WORKLOADS["tiny"]
-    work, dt, threads, sample, phases = bench.cpu_baseline(wl, 1.0, paired)
+    work, dt, threads, sample, phases = bench.cpu_baseline(wl, 1.0, paired, w4a4)
+    assert (phases["quantize"] > 0) == w4a4
     assert dt > 0 and threads >= 1 and work > 0
     assert set(phases) >= {"route", "permute", "decode", "gemm", "combine"}
     assert "routed rows" in sample

@@ -184,9 +184,10 @@ __device__ __forceinline__ void decode_step(uint4 (&A)[RF], const WChunk<RF, KQ>
 // Decode + MFMA over one K chunk staged in `tk`: token T's 16-byte unit c of
 // the chunk sits at element T*KC + 8*(c ^ (T % UPR)), so the MS lanes of a
 // lane group read MS different columns.  The A fragments of k-step s+1 are
-// decoded while the MFMAs of step s run; a scheduling barrier per step
-// bounds the live registers to two steps.  FULL: all TF token fragments hold
-// routed rows.
+// decoded while the MFMAs of step s run.  (A scheduling barrier per step,
+// which kept the compiler from moving work across steps, measured 0.5-1 %
+// slower on the prefill and decode workloads.)  FULL: all TF token
+// fragments hold routed rows.
 template <int MS, int RF, int TF, int KC, bool FULL>
 __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
                                           const uint16_t *tk, const WChunk<RF, KC * MS / 64> &w,
@@ -221,7 +222,6 @@ __device__ __forceinline__ void mma_chunk(typename Mfma<MS>::C (&acc)[RF][TF],
       if (FULL || t < nft)
 #pragma unroll
         for (int f = 0; f < RF; ++f) acc[f][t] = Mfma<MS>::run(A[s & 1][f], B[t], acc[f][t]);
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -66,5 +66,51 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_checker(out_dir: str, verbose: bool = False) -> str:
+    """Builds the library with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host code (the device code is built as usual: the sanitizers
+    apply to the host pass only), linked with tests/abi_checks.c, into
+    out_dir/abi_checks; returns its path.  The program calls every entry
+    point with arguments that the host checks reject before any HIP call,
+    so it runs without a GPU."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".san.o")
+        cmd = [HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", *san,
+               "-c", src, "-o", obj]
+        if src.endswith(".hip"):
+            cmd[1:1] = DEVICE
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host build failed for {src}:\n{r.stderr}")
+        return obj
+
+    srcs = _sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    clang = os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang")
+    driver = os.path.join(ROOT, "tests", "abi_checks.c")
+    dobj = os.path.join(out_dir, "abi_checks.o")
+    r = subprocess.run([clang, "-x", "c", "-O1", "-g", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+                        "-I/opt/rocm/include", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all", "-c", driver, "-o", dobj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed:\n{r.stderr}")
+    exe = os.path.join(out_dir, "abi_checks")
+    rocm_lib = os.path.join(os.path.dirname(HIPCC), "..", "lib")
+    r = subprocess.run([clang + "++", "-fsanitize=address,undefined", "-o", exe, dobj, *objs,
+                        f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {exe}")
+    return exe
+
+
 if __name__ == "__main__":
     build()

@@ -227,3 +227,33 @@ def test_w4a4_chain_1t(lib, name, paired):
         tol_check(f64(out), want, f"{name} W4A4 weighted combine")
     else:
         assert np.array_equal(f64(out), want)
+
+
+@pytest.mark.parametrize("paired", [False, True], ids=["4:8", "paired"])
+def test_w4a4_gather_invalid_perm_entries(lib, paired):
+    """Out-of-range permutation entries give zero rows (plain order) or no
+    store at all (flat order), as with bf16 activations; the other rows are
+    unchanged."""
+    wl = synth.WORKLOADS["decode-30b"]
+    ids, _ = synth.routing(wl)
+    w = lib.tile_weights(pack_workload(lib, wl, 0, paired=paired))
+    x = synth.tokens(wl).cuda()
+    off, perm, inv = lib.route(torch.from_numpy(ids).cuda(), wl.E, wl.k)
+    xq = lib.quantize_activations(x)
+    want = lib.grouped_spgemm_act4(xq, off, w, lib.EPI_NONE, perm=perm, k=wl.k)
+    bad = perm.clone()
+    lost = [0, wl.M // 2, wl.M - 1]
+    bad[lost] = torch.tensor([-1, wl.M, 1 << 30], dtype=torch.int32, device=bad.device)
+    got = lib.grouped_spgemm_act4(xq, off, w, lib.EPI_NONE, perm=bad, k=wl.k)
+    flat = torch.full_like(want, 7)
+    lib.grouped_spgemm_act4(xq, off, w, lib.EPI_NONE | lib.OUT_FLAT, perm=bad, k=wl.k, out=flat)
+    torch.cuda.synchronize()
+    assert not got[lost].any()
+    keep = torch.ones(wl.M, dtype=torch.bool, device=got.device)
+    keep[lost] = False
+    assert torch.equal(got[keep], want[keep])
+    gone = perm[lost].long()                       # flat rows nobody writes now
+    fkeep = torch.ones(wl.M, dtype=torch.bool, device=got.device)
+    fkeep[gone] = False
+    assert bool((flat[~fkeep] == 7).all())
+    assert torch.equal(flat[perm[keep].long()], want[keep])

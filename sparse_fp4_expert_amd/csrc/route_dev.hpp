@@ -62,6 +62,58 @@ __device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, in
   }
 }
 
+// The same two passes over ids[0, M) that one wave holds in registers:
+// lane l, slot j holds ids[64 j + l] (-1 past M or out of range), all
+// loaded at once, so that a short routing (M <= 64 * J) pays one load
+// latency instead of one per 64 ids and pass.
+template <int J>
+__device__ __forceinline__ void wave_load_ids(const int32_t *__restrict__ ids, int M, int E,
+                                              int lane, int (&v)[J]) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = 64 * j + lane;
+    v[j] = i < M ? ids[i] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (v[j] < 0 || v[j] >= E) v[j] = -1;
+}
+
+template <int J>
+__device__ __forceinline__ void wave_count_regs(const int (&v)[J], int M, int nbits,
+                                                uint64_t lt_mask, int *cnt) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (64 * j < M) {   // uniform
+      const int e = v[j];
+      const uint64_t peers = peers_of(e, nbits, __ballot(e >= 0));
+      if (e >= 0 && (peers & lt_mask) == 0) cnt[e] += __popcll(peers);
+    }
+  }
+}
+
+template <int J>
+__device__ __forceinline__ void wave_scatter_regs(const int (&v)[J], int M, int nbits,
+                                                  uint64_t lt_mask, int lane, int *run,
+                                                  int32_t *perm, int32_t *inv_perm) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (64 * j < M) {   // uniform
+      const int i = 64 * j + lane;
+      const int e = v[j];
+      const uint64_t peers = peers_of(e, nbits, __ballot(e >= 0));
+      int row = -1;
+      if (e >= 0) row = run[e] + __popcll(peers & lt_mask);
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && (peers & lt_mask) == 0) run[e] += __popcll(peers);
+      if (i < M) {
+        if (inv_perm) inv_perm[i] = row;
+        if (row >= 0) perm[row] = i;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int id_bits(int E) { return (E > 1) ? 32 - __clz(E - 1) : 0; }
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -449,7 +449,11 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
     if (wave == 0) {
       const uint64_t lt = lanes_below(lane);
       const int nbits = id_bits(E);
-      wave_count(a.ids, 0, M, E, nbits, lt, lane, s_run);
+      // M <= MOESQ_FUSED_ROUTE_MAX_ROWS (checked on the host): every id in
+      // registers after one round of loads
+      int idv[MOESQ_FUSED_ROUTE_MAX_ROWS / 64];
+      wave_load_ids(a.ids, M, E, lane, idv);
+      wave_count_regs(idv, M, nbits, lt, s_run);
       // exclusive prefix of the counts over the experts
       const int per = (E + 63) / 64;
       const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
@@ -470,8 +474,8 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
       }
       if (lane == 63) s_roff[E] = incl;
       __builtin_amdgcn_wave_barrier();
-      wave_scatter(a.ids, 0, M, E, nbits, lt, lane, s_run, s_rperm,
-                   blockIdx.x == 0 ? a.route_inv : nullptr);
+      wave_scatter_regs(idv, M, nbits, lt, lane, s_run, s_rperm,
+                        blockIdx.x == 0 ? a.route_inv : nullptr);
     }
     __syncthreads();
     if (blockIdx.x == 0) {

@@ -52,6 +52,19 @@ def test_fused_matches_two_calls(lib, name, swiglu, paired):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 13, 125, 128])
+def test_fused_row_counts(lib, T):
+    # routed-row counts from one id to the fused maximum (T*k = 1024), ragged
+    # against the 64 ids of a wave
+    wl = synth.WORKLOADS["decode-1t"]
+    print(f"[decode-1t T={T}] fused route + GEMM, M={T * wl.k}", flush=True)
+    ids, _ = synth.routing(wl, T=T, seed=wl.seed + T)
+    w = lib.tile_weights(pack_workload(lib, wl, 1))
+    x = synth.tokens(wl, T=T, K=wl.proj[1][2], seed=wl.seed + T).cuda()
+    _same(lib, torch.from_numpy(ids).cuda(), x, wl.k, w, lib.EPI_NONE, f"T={T}")
+
+
+@pytest.mark.gpu
 def test_fused_fallback_and_empty(lib):
     # tiny: T*k = 128 > 4E = 32 -> the call makes the two separate calls
     wl = synth.WORKLOADS["tiny"]

@@ -62,56 +62,66 @@ __device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, in
   }
 }
 
-// The same two passes over ids[0, M) that one wave holds in registers:
-// lane l, slot j holds ids[64 j + l] (-1 past M or out of range), all
-// loaded at once, so that a short routing (M <= 64 * J) pays one load
-// latency instead of one per 64 ids and pass.
+// The same two passes over a segment ids[base, base + n) that one wave
+// holds in registers: lane l, slot j holds ids[base + 64 j + l] (-1 past
+// the segment or out of range), all loaded at once, so that a short
+// segment (n <= 64 * J) pays one load latency instead of one per 64 ids
+// and pass.  `cnt` / `run` may be int or uint16_t (counts of at most 65535).
 template <int J>
-__device__ __forceinline__ void wave_load_ids(const int32_t *__restrict__ ids, int M, int E,
-                                              int lane, int (&v)[J]) {
+__device__ __forceinline__ void wave_load_ids(const int32_t *__restrict__ ids, int base, int n,
+                                              int E, int lane, int (&v)[J]) {
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int i = 64 * j + lane;
-    v[j] = i < M ? ids[i] : -1;
+    v[j] = i < n ? ids[base + i] : -1;
   }
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (v[j] < 0 || v[j] >= E) v[j] = -1;
 }
 
-template <int J>
-__device__ __forceinline__ void wave_count_regs(const int (&v)[J], int M, int nbits,
-                                                uint64_t lt_mask, int *cnt) {
+template <int J, typename C>
+__device__ __forceinline__ void wave_count_regs(const int (&v)[J], int n, int nbits,
+                                                uint64_t lt_mask, C *cnt) {
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (64 * j < M) {   // uniform
+    if (64 * j < n) {   // uniform
       const int e = v[j];
       const uint64_t peers = peers_of(e, nbits, __ballot(e >= 0));
-      if (e >= 0 && (peers & lt_mask) == 0) cnt[e] += __popcll(peers);
+      if (e >= 0 && (peers & lt_mask) == 0) cnt[e] = (C)(cnt[e] + __popcll(peers));
     }
   }
 }
 
-template <int J>
-__device__ __forceinline__ void wave_scatter_regs(const int (&v)[J], int M, int nbits,
-                                                  uint64_t lt_mask, int lane, int *run,
+template <int J, typename C>
+__device__ __forceinline__ void wave_scatter_regs(const int (&v)[J], int base, int n, int nbits,
+                                                  uint64_t lt_mask, int lane, C *run,
                                                   int32_t *perm, int32_t *inv_perm) {
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    if (64 * j < M) {   // uniform
+    if (64 * j < n) {   // uniform
       const int i = 64 * j + lane;
       const int e = v[j];
       const uint64_t peers = peers_of(e, nbits, __ballot(e >= 0));
       int row = -1;
-      if (e >= 0) row = run[e] + __popcll(peers & lt_mask);
+      if (e >= 0) row = (int)run[e] + __popcll(peers & lt_mask);
       __builtin_amdgcn_wave_barrier();
-      if (e >= 0 && (peers & lt_mask) == 0) run[e] += __popcll(peers);
-      if (i < M) {
-        if (inv_perm) inv_perm[i] = row;
-        if (row >= 0) perm[row] = i;
+      if (e >= 0 && (peers & lt_mask) == 0) run[e] = (C)(run[e] + __popcll(peers));
+      if (i < n) {
+        if (inv_perm) inv_perm[base + i] = row;
+        if (row >= 0) perm[row] = base + i;
       }
     }
   }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
 }
 
 __device__ __forceinline__ int id_bits(int E) { return (E > 1) ? 32 - __clz(E - 1) : 0; }

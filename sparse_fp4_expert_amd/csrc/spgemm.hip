@@ -436,66 +436,18 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
                                               // [E] experts with a partial tile, costly first
 
   if constexpr (!PAIRED) build_group_lut(lut);
-  // Fused routing: the routing plan of the M flat ids (offsets, gather
-  // permutation), built by wave 0 in LDS after the schedule arrays, exactly
-  // as moesq_route builds it (stable counting sort); workgroup 0 also
-  // stores it for the combine.
+  // Fused routing (decode batches): the routing plan of the M flat ids
+  // (offsets and gather permutation), built in LDS after the schedule
+  // arrays, exactly as moesq_route builds it (stable counting sort);
+  // workgroup 0 also stores it for the combine.
   int *const s_roff = s_dyn + spgemm_sched_bytes(E) / 4;   // [E+1]
-  int *const s_run = s_roff + E + 1;                        // [E]
-  int *const s_rperm = s_run + E;                           // [M]
-  if constexpr (ROUTE) {
-    for (int e = tid; e < E; e += WAVES * 64) s_run[e] = 0;
-    __syncthreads();
-    if (wave == 0) {
-      const uint64_t lt = lanes_below(lane);
-      const int nbits = id_bits(E);
-      // M <= MOESQ_FUSED_ROUTE_MAX_ROWS (checked on the host): every id in
-      // registers after one round of loads
-      int idv[MOESQ_FUSED_ROUTE_MAX_ROWS / 64];
-      wave_load_ids(a.ids, M, E, lane, idv);
-      wave_count_regs(idv, M, nbits, lt, s_run);
-      // exclusive prefix of the counts over the experts
-      const int per = (E + 63) / 64;
-      const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-      int sum = 0;
-      for (int e = e0; e < e1; ++e) sum += s_run[e];
-      int incl = sum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      int run = incl - sum;
-      for (int e = e0; e < e1; ++e) {
-        const int c = s_run[e];
-        s_roff[e] = run;
-        s_run[e] = run;
-        run += c;
-      }
-      if (lane == 63) s_roff[E] = incl;
-      __builtin_amdgcn_wave_barrier();
-      wave_scatter_regs(idv, M, nbits, lt, lane, s_run, s_rperm,
-                        blockIdx.x == 0 ? a.route_inv : nullptr);
-    }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int e = tid; e <= E; e += WAVES * 64) a.route_offsets[e] = s_roff[e];
-      for (int r = tid; r < s_roff[E]; r += WAVES * 64) a.route_perm[r] = s_rperm[r];
-    }
-  }
+  int *const s_rperm = s_roff + E + 1;                      // [M]
   // expert row ranges straight from the offsets (clamped to [0, M]); only
   // the item prefix is kept in LDS
   auto off_at = [&](int e) {
     return min(max(ROUTE ? s_roff[e] : a.offsets[e], 0), M);
   };
   auto perm_at = [&](int r) { return ROUTE ? s_rperm[r] : a.perm[r]; };
-  // routed rows per expert; experts outside this launch's row range count as
-  // empty (another launch of the same call takes them)
-  for (int e = tid; e < E; e += WAVES * 64) {
-    const int c = max(0, off_at(e + 1) - off_at(e));
-    s_cnt[e] = (c > a.rows_lo && c <= a.rows_hi) ? c : 0;
-  }
-  __syncthreads();
   // Streaming tiles (16-row fragments) cost about the same whatever their
   // row count (the weight decode dominates), so every token tile of an
   // expert, partial or not, goes in the prefix in expert order, with the
@@ -503,43 +455,130 @@ __attribute__((amdgpu_waves_per_eu(MS == 16 ? 4 : 1, MS == 16 ? 4 : 2))) void sp
   // weights at the same time on one XCD, and the second read hits L2.
   constexpr bool STREAM = MS == 16;
   auto tiles_of = [&](int e) { return STREAM ? (s_cnt[e] + BM - 1) / BM : s_cnt[e] / BM; };
-  if (wave == 0) {
-    // by one wave: prefix of the whole tiles, then the partial tiles bucketed
-    // by fragment count (TF down to 1), experts ascending within a bucket
-    const int per = (E + 63) / 64;
-    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-    auto scan = [&](int v) {   // inclusive prefix over the wave
+  if constexpr (ROUTE) {
+    // Every wave takes a contiguous segment of at most 64 * J ids (M is at
+    // most MOESQ_FUSED_ROUTE_MAX_ROWS, checked on the host) and counts it
+    // per expert into its own row of `cw` (the token buffer, unused until
+    // the first item); one scan over the experts then gives the offsets,
+    // the item prefix and each wave's first routed row per expert, and each
+    // wave scatters its segment.  Segments in wave order and ids in lane
+    // order within a wave keep the sort stable.
+    static_assert(!ROUTE || (STREAM && WAVES * MOESQ_MAX_EXPERTS <= BM * KC),
+                  "fused routing runs on the streaming tile; per-wave counts fit its token buffer");
+    constexpr int NT = WAVES * 64;
+    constexpr int J = (MOESQ_FUSED_ROUTE_MAX_ROWS + NT - 1) / NT;
+    constexpr int EP = (MOESQ_MAX_EXPERTS + NT - 1) / NT;   // experts per thread in the scan
+    __shared__ int s_wtot[2 * WAVES];
+    uint16_t *const cw = tkA;                               // [WAVES][E]
+    uint16_t *const mine = cw + wave * E;
+    const uint64_t lt = lanes_below(lane);
+    const int nbits = id_bits(E);
+    const int seg = 64 * ((M + NT - 1) / NT);
+    const int beg = min(M, wave * seg), len = min(M, beg + seg) - beg;
+    int idv[J];
+    wave_load_ids(a.ids, beg, len, E, lane, idv);
+    for (int i = tid; i < WAVES * E; i += NT) cw[i] = 0;
+    __syncthreads();
+    wave_count_regs(idv, len, nbits, lt, mine);
+    __syncthreads();
+    // experts [tid * EP, tid * EP + EP) of this thread, in expert order
+    int cin[EP], rows_l = 0, tiles_l = 0;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(v, d, 64);
-        if (lane >= d) v += t;
+    for (int q = 0; q < EP; ++q) {
+      const int e = tid * EP + q;
+      int c = 0;
+      if (e < E)
+        for (int w = 0; w < WAVES; ++w) c += cw[w * E + e];
+      cin[q] = c;
+      rows_l += c;
+      const int ci = (c > a.rows_lo && c <= a.rows_hi) ? c : 0;
+      tiles_l += (ci + BM - 1) / BM;
+    }
+    const int rincl = wave_incl_scan(rows_l, lane), tincl = wave_incl_scan(tiles_l, lane);
+    if (lane == 63) {
+      s_wtot[wave] = rincl;
+      s_wtot[WAVES + wave] = tincl;
+    }
+    __syncthreads();
+    int rrun = rincl - rows_l, trun = tincl - tiles_l, rtot = 0, ttot = 0;
+    for (int w = 0; w < WAVES; ++w) {
+      if (w < wave) {
+        rrun += s_wtot[w];
+        trun += s_wtot[WAVES + w];
       }
-      return v;
-    };
-    int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += tiles_of(e);
-    const int incl = scan(sum);
-    int run = incl - sum;
-    for (int e = e0; e < e1; ++e) {
-      s_full[e] = run * a.row_tiles;
-      run += tiles_of(e);
+      rtot += s_wtot[w];
+      ttot += s_wtot[WAVES + w];
     }
-    if (lane == 63) s_full[E] = incl * a.row_tiles;
-    int base = 0;
-    for (int c = STREAM ? 0 : TF; c >= 1; --c) {
-      auto cls = [&](int e) {
-        const int rem = s_cnt[e] % BM;
-        return rem > 0 && (rem + MS - 1) / MS == c;
-      };
-      int cnt = 0;
-      for (int e = e0; e < e1; ++e) cnt += cls(e);
-      const int ci = scan(cnt);
-      int pos = base + ci - cnt;
-      for (int e = e0; e < e1; ++e)
-        if (cls(e)) s_part[pos++] = e;
-      base += __shfl(ci, 63, 64);
+#pragma unroll
+    for (int q = 0; q < EP; ++q) {
+      const int e = tid * EP + q;
+      if (e >= E) break;
+      const int c = cin[q];
+      const int ci = (c > a.rows_lo && c <= a.rows_hi) ? c : 0;
+      s_roff[e] = rrun;
+      s_cnt[e] = ci;
+      s_full[e] = trun * a.row_tiles;
+      trun += (ci + BM - 1) / BM;
+      int r = rrun;   // each wave's first routed row of expert e
+      for (int w = 0; w < WAVES; ++w) {
+        const int t = cw[w * E + e];
+        cw[w * E + e] = (uint16_t)r;
+        r += t;
+      }
+      rrun += c;
     }
-    if (lane == 0) s_npart = base;
+    if (tid == 0) {
+      s_roff[E] = rtot;
+      s_full[E] = ttot * a.row_tiles;
+      s_npart = 0;
+    }
+    __syncthreads();
+    wave_scatter_regs(idv, beg, len, nbits, lt, lane, mine, s_rperm,
+                      blockIdx.x == 0 ? a.route_inv : nullptr);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int e = tid; e <= E; e += NT) a.route_offsets[e] = s_roff[e];
+      for (int r = tid; r < rtot; r += NT) a.route_perm[r] = s_rperm[r];
+    }
+  } else {
+    // routed rows per expert; experts outside this launch's row range count
+    // as empty (another launch of the same call takes them)
+    for (int e = tid; e < E; e += WAVES * 64) {
+      const int c = max(0, off_at(e + 1) - off_at(e));
+      s_cnt[e] = (c > a.rows_lo && c <= a.rows_hi) ? c : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // by one wave: prefix of the whole tiles, then the partial tiles
+      // bucketed by fragment count (TF down to 1), experts ascending within
+      // a bucket
+      const int per = (E + 63) / 64;
+      const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+      int sum = 0;
+      for (int e = e0; e < e1; ++e) sum += tiles_of(e);
+      const int incl = wave_incl_scan(sum, lane);
+      int run = incl - sum;
+      for (int e = e0; e < e1; ++e) {
+        s_full[e] = run * a.row_tiles;
+        run += tiles_of(e);
+      }
+      if (lane == 63) s_full[E] = incl * a.row_tiles;
+      int base = 0;
+      for (int c = STREAM ? 0 : TF; c >= 1; --c) {
+        auto cls = [&](int e) {
+          const int rem = s_cnt[e] % BM;
+          return rem > 0 && (rem + MS - 1) / MS == c;
+        };
+        int cnt = 0;
+        for (int e = e0; e < e1; ++e) cnt += cls(e);
+        const int ci = wave_incl_scan(cnt, lane);
+        int pos = base + ci - cnt;
+        for (int e = e0; e < e1; ++e)
+          if (cls(e)) s_part[pos++] = e;
+        base += __shfl(ci, 63, 64);
+      }
+      if (lane == 0) s_npart = base;
+    }
   }
   __syncthreads();
   const int nfull = s_full[E];
@@ -1244,8 +1283,8 @@ static moesq_status_t launch_one(SpgemmArgs a, hipStream_t stream) {
   constexpr int BM = TF * MS, BN = WAVES * RF * MS;
   auto kern = spgemm_kernel<WAVES, MS, RF, TF, KC, SWIGLU, FMT, ROUTE, ACT4>;
   a.row_tiles = SWIGLU ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-  // schedule arrays, then with fused routing its offsets, cursors and permutation
-  const size_t dyn = spgemm_sched_bytes(a.E) + (ROUTE ? (size_t)(2 * a.E + 1 + a.M) * 4 : 0);
+  // schedule arrays, then with fused routing its offsets and permutation
+  const size_t dyn = spgemm_sched_bytes(a.E) + (ROUTE ? (size_t)(a.E + 1 + a.M) * 4 : 0);
   // upper bound of the item count: every expert may hold one partial tile
   const long long items = ((long long)a.M / BM + std::min(a.E, a.M)) * a.row_tiles;
   // workgroups per CU for this dynamic LDS size (cached per device and size)

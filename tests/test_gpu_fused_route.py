@@ -65,6 +65,35 @@ def test_fused_row_counts(lib, T):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("E,T,k,flat", [(1, 3, 1, False), (7, 4, 7, True), (1000, 128, 8, False),
+                                        (1024, 100, 8, True)])
+def test_fused_expert_counts(lib, E, T, k, flat):
+    # one expert to the largest expert count (the per-wave count table of
+    # the fused routing fills the token buffer at E = 1024), E not a
+    # multiple of the scan's experts per thread, flat and grouped outputs
+    wl = synth.Workload(f"fused-E{E}", E=E, T=T, k=k, proj=(("w", 64, 128),), outliers=False,
+                        bias="gauss", seed=1200 + E, swiglu=False)
+    print(f"[E={E} T={T} k={k} flat={flat}] fused route + GEMM", flush=True)
+    ids, _ = synth.routing(wl)
+    w = lib.tile_weights(pack_workload(lib, wl, 0))
+    x = synth.tokens(wl).cuda()
+    ids_d = torch.from_numpy(ids).cuda()
+    epi = lib.EPI_NONE | (lib.OUT_FLAT if flat else 0)
+    if flat:
+        y1, off1, perm1, inv1 = lib.route_grouped_spgemm(ids_d, x, k, w, epi)
+        off2, perm2, inv2 = lib.route(ids_d, E, k)
+        y2 = lib.grouped_spgemm_gather(x, perm2, k, off2, w, epi)
+        torch.cuda.synchronize()
+        assert torch.equal(off1, off2) and torch.equal(inv1, inv2)
+        assert torch.equal(perm1, perm2) and torch.equal(y1, y2)
+    else:
+        _same(lib, ids_d, x, k, w, epi, wl.name)
+    bad = ids_d.clone()
+    bad[0] = E          # dropped from the plan
+    _same(lib, bad, x, k, w, lib.EPI_NONE, wl.name + " with an invalid id")
+
+
+@pytest.mark.gpu
 def test_fused_fallback_and_empty(lib):
     # tiny: T*k = 128 > 4E = 32 -> the call makes the two separate calls
     wl = synth.WORKLOADS["tiny"]

@@ -49,10 +49,12 @@ def test_quantize_fixture(lib):
     assert q.row_scale.cpu().numpy().tolist() == [float(v) for v in d["g"]]
 
 
-@pytest.mark.parametrize("T,K,seed", [(24, 256, 1), (37, 7168, 2), (8, 32, 3), (130, 2048, 4)])
+@pytest.mark.parametrize("T,K,seed", [(24, 256, 1), (37, 7168, 2), (8, 32, 3), (130, 2048, 4),
+                                        (9, 8192, 5), (7, 8224, 6), (11, 4128, 7)])
 def test_quantize_edge_rows(lib, T, K, seed):
     """Rows spanning 2^-17 to 2^17 in range, outlier channels, a zero row, a
-    zero block, rows of ties and a negative row maximum."""
+    zero block, rows of ties and a negative row maximum; rows whose blocks
+    do not fill the wave's lanes evenly, up to K = 8224."""
     x = pins._act_rows(np.random.default_rng(seed), T=T, K=K)
     xb = torch.from_numpy(x).to(torch.bfloat16)
     q = lib.quantize_activations(xb.cuda())
